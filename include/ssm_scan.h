@@ -1,0 +1,127 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan (S6).
+ *
+ * The operation («Mamba 选择性状态空间模型：亚二次复杂度大语言模型推理工程实践» §2.2, §3.2,
+ * §4.1-§4.2; «Mamba与SSM状态空间模型：一张摘要卡读完万页档案», sections 离散化变换 and
+ * 选择性机制; «AI底层架构的一场革命：Mamba如何用「状态压缩」挑战Transformer的十年统治»,
+ * section "Mamba Block：完整模块结构"):
+ *
+ *   for every (batch b, channel d, state n), over t = 0 .. L-1:
+ *     dt_t  = softplus(delta_t + delta_bias)      (or delta_t + delta_bias if softplus_flag == 0)
+ *     h_t   = exp(dt_t * A) * h_{t-1} + dt_t * B_t * u_t          h_{-1} = h0 (or 0)
+ *     y_t   = (sum_n C_t[n] * h_t[n] + D * u_t) * SiLU(z_t)       (D, z optional)
+ *   and h_last = h_{L-1}.
+ *
+ * Everything is computed in float32 with float32 state; u, delta, B, C, z and
+ * y are stored in io_dtype (float32 or bfloat16), A, D, delta_bias, h0 and
+ * h_last are float32.
+ *
+ * Layouts (all tensors contiguous, innermost index last):
+ *   SSM_LAYOUT_BDL  (per-channel state, one A per (channel, state)):
+ *       u, delta, z, y : (batch, dim, seqlen)
+ *       B, C           : (batch, ngroups, dstate, seqlen)   channel d uses group d / (dim/ngroups)
+ *       A              : (dim, dstate)
+ *       delta_bias, D  : (dim)
+ *   SSM_LAYOUT_BLHP (multi-head state, one scalar A per head; dim = nheads*headdim):
+ *       u, z, y        : (batch, seqlen, nheads, headdim)
+ *       delta          : (batch, seqlen, nheads)
+ *       B, C           : (batch, seqlen, ngroups, dstate)   head h uses group h / (nheads/ngroups)
+ *       A, delta_bias  : (nheads)
+ *       D              : (dim)                               channel d = h*headdim + p
+ *   h0, h_last         : (batch, dim, dstate) float32 in both layouts.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller; the
+ * library keeps none of them after the call returns.  Outputs y and h_last
+ * must not overlap any input or each other.  All tensor base pointers must be
+ * 16-byte aligned.
+ *
+ * Execution: ssm_scan_fwd validates its arguments on the host before any HIP
+ * call, then enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ * default stream) and returns without synchronising.  Faults inside a kernel
+ * surface at the caller's next synchronisation on that stream.  The call is
+ * reentrant; calls on different streams may overlap when each has its own
+ * workspace.
+ *
+ * Workspace: long sequences are split into time segments whose carries are
+ * combined by the library (the chunked scan of «Mamba 选择性状态空间模型» §4.1 and
+ * the state continuation of §7.2).  The scratch they need is
+ * ssm_scan_workspace_size(dims) bytes.  If dims->workspace is NULL and the size is
+ * nonzero, the library allocates it stream-ordered (hipMallocAsync /
+ * hipFreeAsync on `stream`); otherwise dims->workspace must hold at least
+ * that many bytes (SSM_ERR_WORKSPACE if dims->workspace_bytes is smaller).
+ *
+ * Errors: every entry point returns SSM_OK (0) or a negative code; no C++
+ * exception crosses the ABI.  ssm_strerror(code) gives a static message; for
+ * SSM_ERR_HIP it also carries the HIP error text of the failing call (kept
+ * per thread until that thread's next ssm_scan_fwd).
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_LAYOUT_BDL 0
+#define SSM_LAYOUT_BLHP 1
+
+#define SSM_F32 0
+#define SSM_BF16 1
+
+#define SSM_OK 0
+#define SSM_ERR_NULL_ARG -1    /* u, delta, A, B, C, y or dims is NULL */
+#define SSM_ERR_BAD_DIMS -2    /* a size <= 0, nheads*headdim != dim, groups do not divide, ... */
+#define SSM_ERR_UNSUPPORTED -3 /* unknown layout or io_dtype; dstate outside 1..256 */
+#define SSM_ERR_ALIGN -4       /* a tensor pointer is not 16-byte aligned */
+#define SSM_ERR_ALIAS -5       /* y or h_last overlaps an input or each other */
+#define SSM_ERR_WORKSPACE -6   /* caller workspace smaller than ssm_scan_workspace_size */
+#define SSM_ERR_HIP -7         /* a HIP runtime call failed (see ssm_strerror) */
+
+typedef struct ssm_dims {
+  int64_t batch;     /* B >= 1 */
+  int64_t seqlen;    /* L >= 1 */
+  int64_t dim;       /* D = channels (= nheads*headdim for BLHP) */
+  int64_t dstate;    /* N, 1..256 */
+  int64_t nheads;    /* BLHP: H >= 1; BDL: ignored */
+  int64_t headdim;   /* BLHP: P >= 1; BDL: ignored */
+  int64_t ngroups;   /* G >= 1; divides dim (BDL) or nheads (BLHP) */
+  int32_t layout;    /* SSM_LAYOUT_BDL or SSM_LAYOUT_BLHP */
+  int32_t io_dtype;  /* SSM_F32 or SSM_BF16 */
+  void* workspace;          /* optional device scratch, see above */
+  size_t workspace_bytes;   /* its size in bytes */
+} ssm_dims_t;
+
+/*
+ * Selective scan forward.  A, B, C, u, delta, y are required; D, z,
+ * delta_bias, h0 and h_last may be NULL (no skip term, no gate, zero bias,
+ * zero initial state, final state not wanted).  softplus_flag != 0 applies
+ * softplus to delta + delta_bias.  `stream` is a hipStream_t (may be NULL).
+ */
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                 const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream);
+
+/* Bytes of scratch ssm_scan_fwd needs for these dims (0 if none); 0 also for invalid dims. */
+size_t ssm_scan_workspace_size(const ssm_dims_t* dims);
+
+/* Static description of an error code (never NULL). */
+const char* ssm_strerror(int code);
+
+/*
+ * Writes a one-line description of the launch plan chosen for dims
+ * (kernel variant, grid, time segments) into buf; returns SSM_OK or an
+ * error code for invalid dims.  Makes no HIP call.
+ */
+int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int ssm_scan_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

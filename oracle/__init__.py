@@ -13,6 +13,7 @@ from .oracle import (  # noqa: F401
     LAYOUT_BDL,
     LAYOUT_BLHP,
     build,
+    default_threads,
     lib_path,
     scan_f64,
     scan_numpy_f64,

@@ -33,6 +33,15 @@ def lib_path() -> str:
     return _LIB
 
 
+def default_threads() -> int:
+    """Host threads for the oracle: the cores this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def build(verbose: bool = False) -> str:
     """Compile ssm_oracle.c with gcc (plain -O2, IEEE fp64, no fast-math)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", _LIB + ".tmp", _SRC, "-lm"]
@@ -129,7 +138,7 @@ def scan_f64(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, 
     y = np.empty((Bsz, Dm, T) if lay == LAYOUT_BDL else (Bsz, T, H, P), dtype=np.float64)
     h_last = np.empty((Bsz, Dm, N), dtype=np.float64) if want_h_last else None
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = default_threads()
     rc = _load().oracle_scan_f64(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                  _ptr(delta_bias), int(bool(softplus)), _ptr(h0), ctypes.byref(dims),
                                  _ptr(t_out), ctypes.c_int64(0 if t_out is None else T), _ptr(y),

@@ -1,0 +1,230 @@
+// scan_api.cpp -- C ABI of the selective scan: argument validation, launch plan,
+// workspace, error reporting.  Declared in include/ssm_scan.h.
+//
+// Validation runs entirely on the host and makes no HIP call, so every error
+// path can be exercised without a GPU.  The plan splits time into segments only
+// when the rows alone cannot fill the chip (the chunked scan with carries of
+// «Mamba 选择性状态空间模型：亚二次复杂度大语言模型推理工程实践» §4.1 and the state
+// continuation of §7.2).
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "scan_plan.h"
+#include "ssm_scan.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kCUs = 256;   // MI355X compute units
+
+thread_local char g_hip_msg[256] = {0};
+
+int round_up(int64_t x, int64_t m) { return (int)(((x + m - 1) / m) * m); }
+
+// Segment count: enough workgroups for about two per compute unit, but no segment
+// shorter than kMinSeg steps.  SSM_SCAN_SEGMENTS=<n> overrides (tests, tuning).
+int choose_segments(int64_t L, int wgs, int TB, int64_t* seg_len) {
+  constexpr int64_t kMinSeg = 256;
+  int nseg = 1;
+  const char* env = std::getenv("SSM_SCAN_SEGMENTS");
+  if (env && *env) {
+    nseg = std::atoi(env);
+    if (nseg < 1) nseg = 1;
+  } else if (wgs < kCUs) {
+    nseg = (2 * kCUs + wgs - 1) / wgs;
+    const int64_t max_seg = (L + kMinSeg - 1) / kMinSeg;
+    if (nseg > max_seg) nseg = (int)max_seg;
+    if (nseg < 1) nseg = 1;
+  }
+  int64_t len = (L + nseg - 1) / nseg;
+  len = round_up(len, TB);
+  if (len < TB) len = TB;
+  nseg = (int)((L + len - 1) / len);
+  if (nseg > 65535) {  // grid z limit: grow the segments instead
+    len = round_up((L + 65534) / 65535, TB);
+    nseg = (int)((L + len - 1) / len);
+  }
+  *seg_len = len;
+  return nseg;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x0 = (uintptr_t)a, x1 = x0 + na, y0 = (uintptr_t)b, y1 = y0 + nb;
+  return x0 < y1 && y0 < x1;
+}
+
+bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u); }
+
+}  // namespace
+
+int make_plan(const ssm_dims_t* d, Plan* pl) {
+  if (!d || !pl) return SSM_ERR_NULL_ARG;
+  if (d->layout != SSM_LAYOUT_BDL && d->layout != SSM_LAYOUT_BLHP) return SSM_ERR_UNSUPPORTED;
+  if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (d->batch < 1 || d->seqlen < 1 || d->dim < 1 || d->dstate < 1 || d->ngroups < 1) return SSM_ERR_BAD_DIMS;
+  if (d->dstate > 256) return SSM_ERR_UNSUPPORTED;
+  if (d->batch > 65535 || d->dim > (int64_t)1 << 30 || d->seqlen > ((int64_t)1 << 40)) return SSM_ERR_BAD_DIMS;
+  int64_t rows_per_group, groups_or_heads;
+  if (d->layout == SSM_LAYOUT_BDL) {
+    if (d->dim % d->ngroups) return SSM_ERR_BAD_DIMS;
+    rows_per_group = d->dim / d->ngroups;
+    groups_or_heads = d->ngroups;
+  } else {
+    if (d->nheads < 1 || d->headdim < 1 || d->nheads * d->headdim != d->dim) return SSM_ERR_BAD_DIMS;
+    if (d->nheads % d->ngroups) return SSM_ERR_BAD_DIMS;
+    rows_per_group = d->headdim;
+    groups_or_heads = d->nheads;
+  }
+  Plan p;
+  p.layout = d->layout;
+  p.io = d->io_dtype;
+  const int64_t N = d->dstate;
+  p.Npad = N <= 16 ? 16 : N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256;
+  switch (p.Npad) {
+    case 16: p.NS = 2; p.NW = 8; break;
+    case 32: p.NS = 4; p.NW = 8; break;
+    case 64: p.NS = 8; p.NW = 8; break;
+    case 128: p.NS = 16; p.NW = 8; break;
+    default: p.NS = 16; p.NW = 16; break;
+  }
+  p.TB = 16;
+  p.blocks_per_group = (int)((rows_per_group + 63) / 64);
+  const int64_t grid_rows = groups_or_heads * p.blocks_per_group;
+  if (grid_rows > 0x7fffffff) return SSM_ERR_BAD_DIMS;
+  p.grid_rows = (int)grid_rows;
+  const int64_t wgs = grid_rows * d->batch;
+  p.nseg = choose_segments(d->seqlen, (int)(wgs > 0x7fffffff ? 0x7fffffff : wgs), p.TB, &p.seg_len);
+  p.vec_ok = (d->layout == SSM_LAYOUT_BDL) && (d->seqlen % 4 == 0);
+  p.ws_bytes = p.nseg > 1 ? (size_t)2 * (size_t)(p.nseg - 1) * (size_t)d->batch * (size_t)p.Npad *
+                                    (size_t)d->dim * sizeof(float)
+                          : 0;
+  *pl = p;
+  return SSM_OK;
+}
+
+}  // namespace ssm
+
+extern "C" {
+
+int ssm_scan_version(void) { return 100; }
+
+const char* ssm_strerror(int code) {
+  switch (code) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL_ARG: return "a required pointer (u, delta, A, B, C, y, dims) is NULL";
+    case SSM_ERR_BAD_DIMS: return "invalid dimensions (size <= 0, nheads*headdim != dim, or groups do not divide)";
+    case SSM_ERR_UNSUPPORTED: return "unsupported layout, io dtype, or dstate outside 1..256";
+    case SSM_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case SSM_ERR_ALIAS: return "an output overlaps an input or the other output";
+    case SSM_ERR_WORKSPACE: return "workspace is smaller than ssm_scan_workspace_size()";
+    case SSM_ERR_HIP: return ssm::g_hip_msg[0] ? ssm::g_hip_msg : "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+size_t ssm_scan_workspace_size(const ssm_dims_t* dims) {
+  ssm::Plan p;
+  if (ssm::make_plan(dims, &p) != SSM_OK) return 0;
+  return p.ws_bytes;
+}
+
+int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
+  ssm::Plan p;
+  const int rc = ssm::make_plan(dims, &p);
+  if (rc != SSM_OK) return rc;
+  if (buf && buf_len) {
+    std::snprintf(buf, buf_len,
+                  "layout=%s io=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d ws=%zu",
+                  p.layout == SSM_LAYOUT_BDL ? "bdl" : "blhp", p.io == SSM_BF16 ? "bf16" : "f32", p.NS, p.NW, p.TB,
+                  p.Npad, p.grid_rows, (long long)dims->batch, p.nseg, (long long)p.seg_len, (int)p.vec_ok,
+                  p.ws_bytes);
+  }
+  return SSM_OK;
+}
+
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                 const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream) {
+  ssm::g_hip_msg[0] = 0;
+  if (!u || !delta || !A || !B || !C || !y || !dims) return SSM_ERR_NULL_ARG;
+  ssm::Plan pl;
+  int rc = ssm::make_plan(dims, &pl);
+  if (rc != SSM_OK) return rc;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, y, h_last};
+  for (const void* q : ptrs)
+    if (ssm::misaligned(q)) return SSM_ERR_ALIGN;
+
+  // byte extents for the alias check
+  const size_t esz = dims->io_dtype == SSM_BF16 ? 2 : 4;
+  const size_t Bn = (size_t)dims->batch, L = (size_t)dims->seqlen, Dm = (size_t)dims->dim;
+  const size_t N = (size_t)dims->dstate, G = (size_t)dims->ngroups;
+  const bool bdl = dims->layout == SSM_LAYOUT_BDL;
+  const size_t Hn = bdl ? Dm : (size_t)dims->nheads;
+  const size_t n_x = Bn * Dm * L * esz;
+  const size_t n_dt = (bdl ? Bn * Dm * L : Bn * L * Hn) * esz;
+  const size_t n_bc = Bn * G * N * L * esz;
+  const size_t n_A = (bdl ? Dm * N : Hn) * 4;
+  const size_t n_bias = Hn * 4, n_D = Dm * 4, n_state = Bn * Dm * N * 4;
+  struct Range { const void* p; size_t n; };
+  const Range inputs[] = {{u, n_x}, {delta, n_dt}, {A, n_A}, {B, n_bc}, {C, n_bc},
+                          {D, n_D}, {z, n_x}, {delta_bias, n_bias}, {h0, n_state}};
+  for (const Range& r : inputs) {
+    if (ssm::overlaps(y, n_x, r.p, r.n)) return SSM_ERR_ALIAS;
+    if (ssm::overlaps(h_last, n_state, r.p, r.n)) return SSM_ERR_ALIAS;
+  }
+  if (ssm::overlaps(y, n_x, h_last, n_state)) return SSM_ERR_ALIAS;
+
+  void* ws = dims->workspace;
+  bool own_ws = false;
+  if (pl.ws_bytes) {
+    if (ws) {
+      if (dims->workspace_bytes < pl.ws_bytes) return SSM_ERR_WORKSPACE;
+      if (ssm::misaligned(ws)) return SSM_ERR_ALIGN;
+    }
+  }
+  if (pl.ws_bytes && !ws) {
+    hipError_t e = hipMallocAsync(&ws, pl.ws_bytes, (hipStream_t)stream);
+    if (e != hipSuccess) {
+      std::snprintf(ssm::g_hip_msg, sizeof ssm::g_hip_msg, "hipMallocAsync(%zu): %s", pl.ws_bytes,
+                    hipGetErrorString(e));
+      return SSM_ERR_HIP;
+    }
+    own_ws = true;
+  }
+
+  ssm::KParams kp{};
+  kp.u = u; kp.delta = delta; kp.A = A; kp.B = B; kp.C = C; kp.D = D; kp.z = z; kp.bias = delta_bias;
+  kp.h0 = h0; kp.y = y; kp.h_last = h_last;
+  const size_t half = pl.ws_bytes / 2 / sizeof(float);
+  kp.wsP = pl.ws_bytes ? (float*)ws : nullptr;
+  kp.wsH = pl.ws_bytes ? (float*)ws + half : nullptr;
+  kp.L = dims->seqlen; kp.seg_len = pl.seg_len; kp.nseg = pl.nseg;
+  kp.batch = (int)dims->batch; kp.dim = (int)dims->dim; kp.N = (int)dims->dstate; kp.Npad = pl.Npad;
+  kp.H = (int)Hn; kp.P = bdl ? 1 : (int)dims->headdim; kp.G = (int)dims->ngroups;
+  kp.rows_per_group = bdl ? (int)(Dm / G) : (int)dims->headdim;
+  kp.blocks_per_group = pl.blocks_per_group;
+  kp.heads_per_group = bdl ? 1 : (int)(Hn / G);
+  kp.softplus = softplus_flag ? 1 : 0;
+  kp.vec_ok = pl.vec_ok ? 1 : 0;
+
+  const int he = ssm::launch_plan(pl, kp, stream);
+  if (own_ws) {
+    hipError_t e = hipFreeAsync(ws, (hipStream_t)stream);
+    if (he == 0 && e != hipSuccess) {
+      std::snprintf(ssm::g_hip_msg, sizeof ssm::g_hip_msg, "hipFreeAsync: %s", hipGetErrorString(e));
+      return SSM_ERR_HIP;
+    }
+  }
+  if (he != 0) {
+    std::snprintf(ssm::g_hip_msg, sizeof ssm::g_hip_msg, "kernel launch: %s", hipGetErrorString((hipError_t)he));
+    return SSM_ERR_HIP;
+  }
+  return SSM_OK;
+}
+
+}  // extern "C"

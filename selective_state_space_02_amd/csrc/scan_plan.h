@@ -1,0 +1,59 @@
+// scan_plan.h -- launch plan shared by the host API and the kernel launchers.
+//
+// A workgroup owns 64 "rows" (channels of one batch item: one channel group in the
+// (B,D,L) layout, 64 positions of one head in the (B,L,H,P) layout) and all of their
+// states.  The state index is split over NW waves with NS states per lane
+// (NS*NW = Npad >= dstate; padded states carry A = B = C = 0 and stay zero).
+// Time is walked in blocks of TB steps; a sequence may be cut into nseg time
+// segments, in which case an aggregate pass computes each segment's decay product
+// and zero-start end state, and the main pass folds them into its initial state.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include "ssm_scan.h"
+
+namespace ssm {
+
+struct Plan {
+  int layout = 0, io = 0;
+  int NS = 0, NW = 0, TB = 0, Npad = 0;
+  int nseg = 1;
+  int64_t seg_len = 0;
+  int blocks_per_group = 0;  // row blocks of 64 per channel group (BDL) or per head (BLHP)
+  int grid_rows = 0;         // row blocks per batch item
+  bool vec_ok = false;       // 4-step vector loads allowed along time (BDL)
+  size_t ws_bytes = 0;
+};
+
+struct KParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  const float* h0;
+  void* y;
+  float* h_last;
+  float* wsP;   // [seg][b][n][d] decay product of each aggregated segment
+  float* wsH;   // [seg][b][n][d] zero-start end state of each aggregated segment
+  int64_t L, seg_len;
+  int batch, dim, N, Npad, H, P, G;
+  int rows_per_group;    // BDL: dim / G;  BLHP: P
+  int blocks_per_group;  // ceil(rows_per_group / 64)
+  int heads_per_group;   // BLHP: H / G
+  int softplus;
+  int vec_ok;
+  int nseg;
+};
+
+// Validates dims (no HIP call) and fills the plan; returns SSM_OK or an error code.
+int make_plan(const ssm_dims_t* d, Plan* plan);
+
+// Enqueue the kernels of a validated plan.  Returns a hipError_t value (0 = success).
+int launch_plan(const Plan& plan, const KParams& kp, void* stream);
+
+}  // namespace ssm

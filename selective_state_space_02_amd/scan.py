@@ -1,0 +1,190 @@
+"""ctypes binding of libssm_scan.so (include/ssm_scan.h).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of the
+library.  PyTorch allocates and owns device memory (inputs, outputs, workspace)
+and supplies the stream.  There is no fallback: if the library is missing the
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libssm_scan.so")
+
+SSM_LAYOUT_BDL = 0
+SSM_LAYOUT_BLHP = 1
+SSM_F32 = 0
+SSM_BF16 = 1
+
+SSM_OK = 0
+SSM_ERR_NULL_ARG = -1
+SSM_ERR_BAD_DIMS = -2
+SSM_ERR_UNSUPPORTED = -3
+SSM_ERR_ALIGN = -4
+SSM_ERR_ALIAS = -5
+SSM_ERR_WORKSPACE = -6
+SSM_ERR_HIP = -7
+
+EXPORTED = ("ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_strerror", "ssm_scan_describe", "ssm_scan_version")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("dim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64),
+        ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64),
+        ("ngroups", ctypes.c_int64),
+        ("layout", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Open libssm_scan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m selective_state_space_02_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp = ctypes.c_void_p
+        lib.ssm_scan_fwd.restype = ctypes.c_int
+        lib.ssm_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                     ctypes.POINTER(Dims), vp]
+        lib.ssm_scan_workspace_size.restype = ctypes.c_size_t
+        lib.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(Dims)]
+        lib.ssm_strerror.restype = ctypes.c_char_p
+        lib.ssm_strerror.argtypes = [ctypes.c_int]
+        lib.ssm_scan_describe.restype = ctypes.c_int
+        lib.ssm_scan_describe.argtypes = [ctypes.POINTER(Dims), ctypes.c_char_p, ctypes.c_size_t]
+        lib.ssm_scan_version.restype = ctypes.c_int
+        lib.ssm_scan_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load_library().ssm_strerror(int(code)).decode()
+
+
+def make_dims(layout: str, io_dtype: str, batch: int, seqlen: int, dim: int, dstate: int,
+              nheads: int = 0, headdim: int = 0, ngroups: int = 1) -> Dims:
+    return Dims(batch, seqlen, dim, dstate, nheads, headdim, ngroups,
+                SSM_LAYOUT_BDL if layout == "bdl" else SSM_LAYOUT_BLHP,
+                SSM_BF16 if io_dtype == "bf16" else SSM_F32, None, 0)
+
+
+def workspace_size(dims: Dims) -> int:
+    return int(load_library().ssm_scan_workspace_size(ctypes.byref(dims)))
+
+
+def describe(dims: Dims) -> str:
+    buf = ctypes.create_string_buffer(256)
+    rc = load_library().ssm_scan_describe(ctypes.byref(dims), buf, 256)
+    if rc != SSM_OK:
+        raise ValueError(strerror(rc))
+    return buf.value.decode()
+
+
+def call_raw(u, delta, A, B, C, D, z, delta_bias, softplus, h0, y, h_last, dims: Dims, stream=None) -> int:
+    """Direct ABI call with integer addresses (None = NULL).  Returns the status code."""
+    return int(load_library().ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, int(bool(softplus)), h0, y,
+                                          h_last, ctypes.byref(dims), stream))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype, shape, device):
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def ssm_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                 D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                 delta_bias: Optional[torch.Tensor] = None, softplus: bool = True,
+                 h0: Optional[torch.Tensor] = None, *, layout: str = "bdl", ngroups: int = 1,
+                 y: Optional[torch.Tensor] = None, h_last: Optional[torch.Tensor] = None,
+                 want_h_last: bool = True, workspace: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Selective scan on the GPU.  Shapes as in include/ssm_scan.h; returns (y, h_last)."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("ssm_scan_fwd runs on the GPU: tensors must be on a cuda device")
+    io = u.dtype
+    if io not in (torch.float32, torch.bfloat16):
+        raise TypeError("u must be float32 or bfloat16")
+    if layout == "bdl":
+        Bsz, Dm, L = u.shape
+        G, N = B.shape[1], B.shape[2]
+        H, P = 0, 0
+        shapes = dict(delta=(Bsz, Dm, L), A=(Dm, N), B=(Bsz, G, N, L), bias=(Dm,), x=(Bsz, Dm, L))
+    elif layout == "blhp":
+        Bsz, L, H, P = u.shape
+        Dm = H * P
+        G, N = B.shape[2], B.shape[3]
+        shapes = dict(delta=(Bsz, L, H), A=(H,), B=(Bsz, L, G, N), bias=(H,), x=(Bsz, L, H, P))
+    else:
+        raise ValueError(layout)
+    if G != ngroups:
+        ngroups = G
+    f32 = torch.float32
+    _check(delta, "delta", io, shapes["delta"], dev)
+    _check(A, "A", f32, shapes["A"], dev)
+    _check(B, "B", io, shapes["B"], dev)
+    _check(C, "C", io, shapes["B"], dev)
+    _check(D, "D", f32, (Dm,), dev)
+    _check(z, "z", io, shapes["x"], dev)
+    _check(delta_bias, "delta_bias", f32, shapes["bias"], dev)
+    _check(h0, "h0", f32, (Bsz, Dm, N), dev)
+    if y is None:
+        y = torch.empty(shapes["x"], dtype=io, device=dev)
+    _check(y, "y", io, shapes["x"], dev)
+    if h_last is None and want_h_last:
+        h_last = torch.empty((Bsz, Dm, N), dtype=f32, device=dev)
+    _check(h_last, "h_last", f32, (Bsz, Dm, N), dev)
+    dims = make_dims(layout, "bf16" if io == torch.bfloat16 else "f32", Bsz, L, Dm, N, H, P, ngroups)
+    need = int(lib.ssm_scan_workspace_size(ctypes.byref(dims)))
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        dims.workspace = workspace.data_ptr()
+        dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                          int(bool(softplus)), _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims),
+                          ctypes.c_void_p(st.cuda_stream))
+    if rc != SSM_OK:
+        raise RuntimeError(f"ssm_scan_fwd failed ({rc}): {strerror(rc)}")
+    return y, h_last
+
+
+def ssm_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None, **kw):
+    """Convenience wrapper: returns (y, h_last)."""
+    return ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, softplus, h0, **kw)

