@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan (S6) forward on one MI355X.
+
+One step = one ssm_scan_fwd call over the whole workload batch (all of the
+path: step size, discretisation, recurrence, readout, skip, gate, final
+state), inputs already resident in HBM.  Three input sets are rotated so the
+256 MB Infinity Cache cannot serve a repeated working set.
+
+Prints ONE JSON line: metric/value (elements B*L*D*N per second), the
+roofline of the scan kernel (measured live with HIP events on the launch
+stream), and the fp64 CPU oracle timed on a bounded sample on host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan elements/s (B·L·D·N) + achieved HBM GB/s vs MI355X peak"
+DEFAULT_WORKLOAD = "mamba2p8b_layer"
+
+# MI355X figures used for the rooflines (vendor numbers).
+HBM_PEAK_GBS = 8000.0
+CUS, SIMDS, LANES_PER_CLK, CLOCK_HZ = 256, 4, 32, 2.4e9
+VALU_SLOT_PEAK = CUS * SIMDS * LANES_PER_CLK * CLOCK_HZ       # 78.64e12 fp32 lane-ops/s (= 157.3 TFLOP/s FMA)
+TRANS_SLOTS = 4                                               # exp2/log2/rcp issue at 1/4 of the fp32 rate
+
+# Algorithmic work of the path, in fp32 VALU slots.
+#  per (b,d,t,n): exp(dt*A) [1 mul + 1 transcendental], dt*u*B [1 mul], h update [1 fma], readout [1 fma]
+#  per (b,d,t)  : softplus [bias add, 1+e add, exp, log], dt*u [mul], D*u [fma],
+#                 SiLU gate [exp, 1+e add, rcp, z*s mul, y*s mul]
+#  multi-head layout: exp(dt*A) is per (b,t,h), so per element only dt*u*B, h update, readout.
+def algorithmic_slots(case) -> float:
+    Bsz, L, Dm, N = case.batch, case.seqlen, case.dim, case.dstate
+    has_z = case.tensors["z"] is not None
+    per_row_step = (2 + 2 * TRANS_SLOTS) + 2 + ((3 + 2 * TRANS_SLOTS) if has_z else 0)
+    if case.layout == "bdl":
+        per_elem = 4 + TRANS_SLOTS
+        return Bsz * L * Dm * (N * per_elem + per_row_step)
+    per_elem = 3
+    per_head_step = (2 + 2 * TRANS_SLOTS) + (1 + TRANS_SLOTS)  # softplus + exp(dt*A) per (b,t,h)
+    per_chan_step = 2 + ((3 + 2 * TRANS_SLOTS) if has_z else 0)
+    return Bsz * L * (Dm * (N * per_elem + per_chan_step) + case.nheads * per_head_step)
+
+
+def algorithmic_bytes(case) -> int:
+    """Each input read once, each output written once; B/C once per (b, t)."""
+    T = case.tensors
+    total = 0
+    for k in ("u", "delta", "B", "C", "z", "A", "D", "delta_bias", "h0"):
+        if T[k] is not None:
+            total += T[k].numel() * T[k].element_size()
+    total += T["u"].numel() * T["u"].element_size()                  # y
+    total += case.batch * case.dim * case.dstate * 4                 # h_last
+    return total
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("selective_state_space_02_amd/csrc/scan_kernels.hip", "selective_state_space_02_amd/csrc/scan_api.cpp",
+              "selective_state_space_02_amd/csrc/scan_plan.h"):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they match this kernel."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float = 12.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload: the first
+    batch items (whole) or, if one item is already over budget, the first channels of
+    item 0, always over the full sequence.  Returns the dict for the JSON line."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    T = case.tensors
+    io = case.io_dtype
+
+    def np_io(t):
+        if t is None:
+            return None
+        t = t.contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if io == "bf16" else t.numpy()
+
+    def run(nb, nch):
+        """nb batch items; nch channels (BDL) or nch // headdim heads (BLHP)."""
+        f = lambda t: None if t is None else t.contiguous().numpy()
+        if case.layout == "bdl":
+            x = lambda t: None if t is None else t[:nb, :nch]
+            args = (np_io(x(T["u"])), np_io(x(T["delta"])), f(T["A"][:nch]), np_io(T["B"][:nb]), np_io(T["C"][:nb]),
+                    f(None if T["D"] is None else T["D"][:nch]), np_io(x(T["z"])),
+                    f(None if T["delta_bias"] is None else T["delta_bias"][:nch]), case.softplus,
+                    f(None if T["h0"] is None else T["h0"][:nb, :nch]))
+            elems = nb * case.seqlen * nch * case.dstate
+        else:
+            nh = max(1, nch // case.headdim)
+            x = lambda t: None if t is None else t[:nb, :, :nh]
+            nc = nh * case.headdim
+            args = (np_io(x(T["u"])), np_io(x(T["delta"])), f(T["A"][:nh]), np_io(T["B"][:nb]), np_io(T["C"][:nb]),
+                    f(None if T["D"] is None else T["D"][:nc]), np_io(x(T["z"])),
+                    f(None if T["delta_bias"] is None else T["delta_bias"][:nh]), case.softplus,
+                    f(None if T["h0"] is None else T["h0"][:nb, :nc]))
+            elems = nb * case.seqlen * nc * case.dstate
+        threads = oracle.default_threads()
+        t0 = time.perf_counter()
+        oracle.scan_f64(*args, nthreads=threads, layout=case.layout, io_dtype=io, ngroups=case.ngroups)
+        return time.perf_counter() - t0, elems, threads
+
+    probe_ch = 64 if case.layout == "bdl" else case.headdim
+    dt, el, _ = run(1, probe_ch)
+    rate = el / max(dt, 1e-6)
+    per_item = case.seqlen * case.dim * case.dstate
+    nb = int(min(case.batch, max(1, rate * budget_s // per_item)))
+    if rate * budget_s >= per_item:
+        nch, what = case.dim, f"batch items 0..{nb - 1} of {case.batch} (all channels)"
+    else:
+        nch = int(max(probe_ch, rate * budget_s / (case.seqlen * case.dstate)))
+        if case.layout == "blhp":
+            nch = max(case.headdim, (nch // case.headdim) * case.headdim)
+        nch = min(nch, case.dim)
+        what = f"batch item 0, first {nch} of {case.dim} channels"
+    dt, el, threads = run(nb, nch)
+    return {"value": el / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}, all {case.seqlen} steps, {case.dstate} states: {el:.3e} elements in {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rotate", type=int, default=3, help="input sets rotated through (defeats the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run only a plain copy of this many MiB (counter calibration), then exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the scan shards over "
+              "batch x channel with no communication); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from selective_state_space_02_amd import scan
+    from selective_state_space_02_amd.inputs import make_config
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4}))
+        return
+
+    case = make_config(args.workload)
+    sets = []
+    for i in range(max(1, args.rotate)):
+        T = {k: (None if v is None else v.to(dev)) for k, v in case.tensors.items()}
+        y = torch.empty_like(T["u"])
+        h = torch.empty((case.batch, case.dim, case.dstate), dtype=torch.float32, device=dev)
+        sets.append((T, y, h))
+    dims = scan.make_dims(case.layout, case.io_dtype, case.batch, case.seqlen, case.dim, case.dstate,
+                          case.nheads, case.headdim, case.ngroups)
+    ws_bytes = scan.workspace_size(dims)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    plan = scan.describe(dims)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        T, y, h = sets[i % len(sets)]
+        scan.ssm_scan_fwd(T["u"], T["delta"], T["A"], T["B"], T["C"], T["D"], T["z"], T["delta_bias"],
+                          case.softplus, T["h0"], layout=case.layout, y=y, h_last=h, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, synchronised on both sides; per-launch HIP events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+
+    ms_per_step = wall * 1e3 / args.steps
+    elements = case.elements
+    value = elements / (ms_per_step * 1e-3)
+
+    slots = algorithmic_slots(case)
+    achieved = slots / (launch_ms * 1e-3) / 1e12
+    peak = VALU_SLOT_PEAK / 1e12
+    abytes = algorithmic_bytes(case)
+    traffic = load_traffic(args.workload)
+    hbm_gbs = abytes / (launch_ms * 1e-3) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "layout": case.layout, "io_dtype": case.io_dtype, "batch": case.batch,
+                   "seqlen": case.seqlen, "dim": case.dim, "dstate": case.dstate, "nheads": case.nheads,
+                   "headdim": case.headdim, "ngroups": case.ngroups, "plan": plan},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel_ms": launch_ms, "algorithmic_ops_per_launch": slots,
+                     "op": "fp32 VALU lane-issue slot (transcendental = 4)"},
+        "hbm": {"algorithmic_bytes_per_launch": abytes, "achieved_GBs": hbm_gbs, "peak_GBs": HBM_PEAK_GBS,
+                "frac": hbm_gbs / HBM_PEAK_GBS},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

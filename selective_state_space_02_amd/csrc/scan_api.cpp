@@ -25,31 +25,32 @@ thread_local char g_hip_msg[256] = {0};
 
 int round_up(int64_t x, int64_t m) { return (int)(((x + m - 1) / m) * m); }
 
-// Segment count: enough workgroups for about two per compute unit, but no segment
-// shorter than kMinSeg steps.  SSM_SCAN_SEGMENTS=<n> overrides (tests, tuning).
-int choose_segments(int64_t L, int wgs, int TB, int64_t* seg_len) {
+// Segment count: enough parallel units (waves for the row-group kernel, workgroups
+// otherwise) to fill the chip, but no segment shorter than kMinSeg steps.
+// SSM_SCAN_SEGMENTS=<n> overrides (tests, tuning).
+int choose_segments(int64_t L, int64_t units, int64_t target, int TB, int64_t* seg_len) {
   constexpr int64_t kMinSeg = 256;
-  int nseg = 1;
+  int64_t nseg = 1;
   const char* env = std::getenv("SSM_SCAN_SEGMENTS");
   if (env && *env) {
     nseg = std::atoi(env);
     if (nseg < 1) nseg = 1;
-  } else if (wgs < kCUs) {
-    nseg = (2 * kCUs + wgs - 1) / wgs;
+  } else if (units < target / 2) {
+    nseg = (target + units - 1) / units;
     const int64_t max_seg = (L + kMinSeg - 1) / kMinSeg;
-    if (nseg > max_seg) nseg = (int)max_seg;
+    if (nseg > max_seg) nseg = max_seg;
     if (nseg < 1) nseg = 1;
   }
   int64_t len = (L + nseg - 1) / nseg;
   len = round_up(len, TB);
   if (len < TB) len = TB;
-  nseg = (int)((L + len - 1) / len);
+  nseg = (L + len - 1) / len;
   if (nseg > 65535) {  // grid z limit: grow the segments instead
     len = round_up((L + 65534) / 65535, TB);
-    nseg = (int)((L + len - 1) / len);
+    nseg = (L + len - 1) / len;
   }
   *seg_len = len;
-  return nseg;
+  return (int)nseg;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -92,13 +93,29 @@ int make_plan(const ssm_dims_t* d, Plan* pl) {
     case 128: p.NS = 16; p.NW = 8; break;
     default: p.NS = 16; p.NW = 16; break;
   }
-  p.TB = 16;
-  p.blocks_per_group = (int)((rows_per_group + 63) / 64);
-  const int64_t grid_rows = groups_or_heads * p.blocks_per_group;
-  if (grid_rows > 0x7fffffff) return SSM_ERR_BAD_DIMS;
-  p.grid_rows = (int)grid_rows;
-  const int64_t wgs = grid_rows * d->batch;
-  p.nseg = choose_segments(d->seqlen, (int)(wgs > 0x7fffffff ? 0x7fffffff : wgs), p.TB, &p.seg_len);
+  // Per-channel layout with up to 32 states: one wave per 8 channels, no barriers.
+  p.kernel = (d->layout == SSM_LAYOUT_BDL && p.Npad <= 32) ? 1 : 0;
+  int64_t units, target;
+  if (p.kernel == 1) {
+    p.NS = p.Npad / 8;
+    p.NW = 1;
+    p.TB = 32;
+    p.blocks_per_group = (int)((rows_per_group + 7) / 8);
+    const int64_t row_blocks = groups_or_heads * p.blocks_per_group;
+    p.grid_rows = (int)((row_blocks + 3) / 4);
+    units = row_blocks * d->batch;            // waves
+    target = 4 * kCUs * 2;                    // two waves per SIMD
+  } else {
+    p.TB = 16;
+    p.blocks_per_group = (int)((rows_per_group + 63) / 64);
+    const int64_t grid_rows = groups_or_heads * p.blocks_per_group;
+    if (grid_rows > 0x7fffffff) return SSM_ERR_BAD_DIMS;
+    p.grid_rows = (int)grid_rows;
+    units = grid_rows * d->batch;             // workgroups
+    target = 2 * kCUs;
+  }
+  if ((int64_t)p.grid_rows > 0x7fffffff) return SSM_ERR_BAD_DIMS;
+  p.nseg = choose_segments(d->seqlen, units, target, p.TB, &p.seg_len);
   p.vec_ok = (d->layout == SSM_LAYOUT_BDL) && (d->seqlen % 4 == 0);
   p.ws_bytes = p.nseg > 1 ? (size_t)2 * (size_t)(p.nseg - 1) * (size_t)d->batch * (size_t)p.Npad *
                                     (size_t)d->dim * sizeof(float)
@@ -139,8 +156,8 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
   if (rc != SSM_OK) return rc;
   if (buf && buf_len) {
     std::snprintf(buf, buf_len,
-                  "layout=%s io=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d ws=%zu",
-                  p.layout == SSM_LAYOUT_BDL ? "bdl" : "blhp", p.io == SSM_BF16 ? "bf16" : "f32", p.NS, p.NW, p.TB,
+                  "kernel=%s layout=%s io=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d ws=%zu",
+                  p.kernel == 1 ? "rowgroup" : "workgroup", p.layout == SSM_LAYOUT_BDL ? "bdl" : "blhp", p.io == SSM_BF16 ? "bf16" : "f32", p.NS, p.NW, p.TB,
                   p.Npad, p.grid_rows, (long long)dims->batch, p.nseg, (long long)p.seg_len, (int)p.vec_ok,
                   p.ws_bytes);
   }
@@ -210,6 +227,8 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   kp.blocks_per_group = pl.blocks_per_group;
   kp.heads_per_group = bdl ? 1 : (int)(Hn / G);
   kp.softplus = softplus_flag ? 1 : 0;
+  kp.zsrc = z ? z : u;
+  kp.has_z = z ? 1 : 0;
   kp.vec_ok = pl.vec_ok ? 1 : 0;
 
   const int he = ssm::launch_plan(pl, kp, stream);

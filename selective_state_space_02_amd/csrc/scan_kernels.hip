@@ -41,41 +41,81 @@ constexpr float kLn2 = 0.6931471805599453f;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- element I/O
+// Global loads are issued as raw bits one time block ahead (so their latency hides
+// behind the recurrence of the current block) and converted to fp32 only when used.
+template <int BYTES> struct RawT;
+template <> struct RawT<2> { using T = uint16_t; };
+template <> struct RawT<4> { using T = uint32_t; };
+template <> struct RawT<8> { using T = uint2; };
+template <> struct RawT<16> { using T = uint4; };
+
 struct F32IO {
+  using S = uint32_t;                                  // storage bits of one element
   static constexpr int kBytes = 4;
-  __device__ static float ld(const void* p, int64_t i) { return ((const float*)p)[i]; }
-  __device__ static void st(void* p, int64_t i, float v) { ((float*)p)[i] = v; }
-  // four consecutive elements, i multiple of 4, 16-byte aligned
-  __device__ static void ld4(const void* p, int64_t i, float v[4]) {
-    const float4 q = *(const float4*)((const float*)p + i);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  __device__ static S ld_bits(const void* p, int64_t i) { return ((const uint32_t*)p)[i]; }
+  __device__ static float cvt(S v) { return __uint_as_float(v); }
+  template <int V> __device__ static void unpack(const typename RawT<4 * V>::T& r, float* o) {
+    if constexpr (V == 1) { o[0] = __uint_as_float(r); }
+    if constexpr (V == 2) { o[0] = __uint_as_float(r.x); o[1] = __uint_as_float(r.y); }
+    if constexpr (V == 4) {
+      o[0] = __uint_as_float(r.x); o[1] = __uint_as_float(r.y);
+      o[2] = __uint_as_float(r.z); o[3] = __uint_as_float(r.w);
+    }
   }
-  __device__ static void st4(void* p, int64_t i, const float v[4]) {
-    *(float4*)((float*)p + i) = make_float4(v[0], v[1], v[2], v[3]);
+  template <int V> __device__ static void pack_elem(typename RawT<4 * V>::T& r, int q, S v) {
+    if constexpr (V == 1) { r = v; }
+    if constexpr (V == 2) { if (q == 0) r.x = v; else r.y = v; }
+    if constexpr (V == 4) { if (q == 0) r.x = v; else if (q == 1) r.y = v; else if (q == 2) r.z = v; else r.w = v; }
+  }
+  __device__ static void st(void* p, int64_t i, float v) { ((float*)p)[i] = v; }
+  template <int V> __device__ static void stv(void* p, int64_t i, const float* v) {
+    if constexpr (V == 1) ((float*)p)[i] = v[0];
+    if constexpr (V == 2) *(float2*)((float*)p + i) = make_float2(v[0], v[1]);
+    if constexpr (V == 4) *(float4*)((float*)p + i) = make_float4(v[0], v[1], v[2], v[3]);
   }
 };
 
 struct BF16IO {
+  using S = uint16_t;
   static constexpr int kBytes = 2;
-  __device__ static float ld(const void* p, int64_t i) {
-    return __uint_as_float(((uint32_t)((const uint16_t*)p)[i]) << 16);
+  __device__ static S ld_bits(const void* p, int64_t i) { return ((const uint16_t*)p)[i]; }
+  __device__ static float cvt(S v) { return __uint_as_float(((uint32_t)v) << 16); }
+  template <int V> __device__ static void unpack(const typename RawT<2 * V>::T& r, float* o) {
+    if constexpr (V == 1) { o[0] = __uint_as_float(((uint32_t)r) << 16); }
+    if constexpr (V == 2) { o[0] = __uint_as_float(r << 16); o[1] = __uint_as_float(r & 0xffff0000u); }
+    if constexpr (V == 4) {
+      o[0] = __uint_as_float(r.x << 16); o[1] = __uint_as_float(r.x & 0xffff0000u);
+      o[2] = __uint_as_float(r.y << 16); o[3] = __uint_as_float(r.y & 0xffff0000u);
+    }
+    if constexpr (V == 8) {
+      o[0] = __uint_as_float(r.x << 16); o[1] = __uint_as_float(r.x & 0xffff0000u);
+      o[2] = __uint_as_float(r.y << 16); o[3] = __uint_as_float(r.y & 0xffff0000u);
+      o[4] = __uint_as_float(r.z << 16); o[5] = __uint_as_float(r.z & 0xffff0000u);
+      o[6] = __uint_as_float(r.w << 16); o[7] = __uint_as_float(r.w & 0xffff0000u);
+    }
+  }
+  template <int V> __device__ static void pack_elem(typename RawT<2 * V>::T& r, int q, S v) {
+    if constexpr (V == 1) { r = v; }
+    if constexpr (V == 2) { r |= ((uint32_t)v) << (16 * q); }
+    if constexpr (V == 4) {
+      if (q < 2) r.x |= ((uint32_t)v) << (16 * q); else r.y |= ((uint32_t)v) << (16 * (q - 2));
+    }
   }
   __device__ static void st(void* p, int64_t i, float v) {
     bf16x2 w = {(__bf16)v, (__bf16)0.0f};
     ((uint16_t*)p)[i] = (uint16_t)(__builtin_bit_cast(uint32_t, w) & 0xffffu);
   }
-  // four consecutive elements, i multiple of 4, 8-byte aligned
-  __device__ static void ld4(const void* p, int64_t i, float v[4]) {
-    const uint2 q = *(const uint2*)((const uint16_t*)p + i);
-    v[0] = __uint_as_float(q.x << 16);
-    v[1] = __uint_as_float(q.x & 0xffff0000u);
-    v[2] = __uint_as_float(q.y << 16);
-    v[3] = __uint_as_float(q.y & 0xffff0000u);
-  }
-  __device__ static void st4(void* p, int64_t i, const float v[4]) {
-    bf16x2 a = {(__bf16)v[0], (__bf16)v[1]};
-    bf16x2 b = {(__bf16)v[2], (__bf16)v[3]};
-    *(uint2*)((uint16_t*)p + i) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+  template <int V> __device__ static void stv(void* p, int64_t i, const float* v) {
+    if constexpr (V == 1) st(p, i, v[0]);
+    if constexpr (V == 2) {
+      bf16x2 a = {(__bf16)v[0], (__bf16)v[1]};
+      *(uint32_t*)((uint16_t*)p + i) = __builtin_bit_cast(uint32_t, a);
+    }
+    if constexpr (V == 4) {
+      bf16x2 a = {(__bf16)v[0], (__bf16)v[1]};
+      bf16x2 c = {(__bf16)v[2], (__bf16)v[3]};
+      *(uint2*)((uint16_t*)p + i) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c));
+    }
   }
 };
 
@@ -99,20 +139,36 @@ __device__ __forceinline__ float silu_f(float z) {
 // ---------------------------------------------------------------- the kernel
 // LAYOUT 0: (B,D,L) per-channel A;  LAYOUT 1: (B,L,H,P) per-head scalar A.
 // MODE 0: main pass (readout, gate, y, h_last);  MODE 1: segment aggregates.
-template <int LAYOUT, typename IO, int NS, int NW, int TB, int MODE>
+// VECOK: the sequence length is a multiple of the chunk width, so a chunk never
+// straddles the end of a row and can be moved with one vector load / store.
+template <int NT, int TB>
+constexpr int chunk_width() { return (64 * TB >= 4 * NT) ? 4 : (64 * TB >= 2 * NT) ? 2 : 1; }
+
+template <int LAYOUT, typename IO, int NS, int NW, int TB, int MODE, bool VECOK>
 __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
   constexpr int NT = NW * 64;          // threads per workgroup
   constexpr int TP = TB + 4;           // padded time stride of per-row LDS tiles
   constexpr int NPAD = NS * NW;
   static_assert(TB % 4 == 0, "TB must be a multiple of 4");
+  using S = typename IO::S;
 
-  // per-(row, t) step size and dt*u.  BDL: [row][TP] (time contiguous, read 4 at a time);
-  // BLHP: dt and a are per (t) only, dt*u is [t][65].
+  // BDL phase A/C: a chunk is VEC consecutive steps of one row, row-major over the tile
+  constexpr int VEC = chunk_width<NT, TB>();
+  constexpr int CH_PER_ROW = TB / VEC;
+  constexpr int NCHUNK = 64 * CH_PER_ROW;
+  constexpr int CPT = (NCHUNK + NT - 1) / NT;
+  using RawV = typename RawT<VEC * IO::kBytes>::T;
+  // BLHP phase A/C: thread (lane = position, tq = wave) owns steps tq, tq + NW, ...
+  constexpr int TPT = (TB + NW - 1) / NW;
+  // B/C staging: NBC values per thread (B then C)
+  constexpr int NBCV = (MODE == 0 ? 2 : 1) * NPAD * TB;
+  constexpr int NBC = (NBCV + NT - 1) / NT;
+
   __shared__ __attribute__((aligned(16))) float s_dt[LAYOUT == 0 ? 64 * TP : TB];
   __shared__ __attribute__((aligned(16))) float s_a[LAYOUT == 0 ? 4 : TB];
   __shared__ __attribute__((aligned(16))) float s_du[LAYOUT == 0 ? 64 * TP : TB * 65];
   __shared__ __attribute__((aligned(16))) float s_bc[TB * NPAD * 2];   // [t][w][B0..B_NS-1, C0..C_NS-1]
-  __shared__ __attribute__((aligned(16))) float s_yp[MODE == 0 ? (LAYOUT == 0 ? NW * 64 * TP : NW * TB * 65) : 1];
+  __shared__ __attribute__((aligned(16))) float s_yp[MODE == 0 ? (LAYOUT == 0 ? NW * 64 * TP : NW * TB * 65) : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,6 +178,7 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
   const int64_t L = p.L;
   const int64_t t_seg0 = (int64_t)seg * p.seg_len;
   const int64_t t_seg1 = min(L, t_seg0 + p.seg_len);
+  constexpr bool vec_ok = VECOK;
 
   // ---- which rows this workgroup owns
   const int grp_blk = blockIdx.x / p.blocks_per_group;   // channel group (BDL) or head (BLHP)
@@ -161,20 +218,93 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
       }
     }
   }
-  float sum_dt = 0.0f;   // MODE 1, BDL: per-row sum of step sizes over the segment
+  float sum_dt = 0.0f;   // MODE 1: sum of step sizes over the segment (per row / per head)
 
-  // ---- per-thread chunk bookkeeping for phases A and C
-  // BDL: chunk = 4 consecutive steps of one row; chunks are row-major so that 16
-  //      consecutive lanes read one row's TB steps contiguously.
-  constexpr int CH_PER_ROW = TB / 4;
-  constexpr int NCHUNK = 64 * CH_PER_ROW;
-  constexpr int CPT = (NCHUNK + NT - 1) / NT;
-  // BLHP: thread (lane = position p, tq = tid / 64) owns steps tq, tq+NW, ...
-  constexpr int TPT = (TB + NW - 1) / NW;
-  float keep_u[LAYOUT == 0 ? CPT * 4 : TPT];
-  float keep_z[LAYOUT == 0 ? CPT * 4 : TPT];
+  // ---- registers carried across phases and blocks
+  RawV pf_dt[LAYOUT == 0 ? CPT : 1], pf_u[LAYOUT == 0 ? CPT : 1], pf_z[LAYOUT == 0 ? CPT : 1];
+  S pm_dt[LAYOUT == 1 ? TPT : 1], pm_u[LAYOUT == 1 ? TPT : 1], pm_z[LAYOUT == 1 ? TPT : 1];
+  S pf_bc[NBC];
+  float keep_u[LAYOUT == 0 ? CPT * VEC : TPT];
+  float keep_z[LAYOUT == 0 ? CPT * VEC : TPT];
 
+  // Issue the global loads of the block starting at tb as raw bits.  Loads are
+  // unconditional: an out-of-range element is fetched from a clamped in-bounds
+  // address and masked when phase A consumes it, so no register is written twice
+  // while a load is in flight and the wait for the data falls in the next phase A.
+  auto issue_loads = [&](int64_t tb) {
+    const int nvalid = (int)min((int64_t)TB, t_seg1 - tb);
+    if (LAYOUT == 0) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int c = tid + k * NT;
+        int r = c / CH_PER_ROW;
+        int t0 = (c % CH_PER_ROW) * VEC;
+        if constexpr (vec_ok) {
+          // a chunk never straddles the end of a row, so a full vector load stays in bounds
+          if (!(c < NCHUNK && r < rows_in && tb + t0 < L)) { r = 0; t0 = 0; }
+          const int64_t base = ((int64_t)b * p.dim + d_base + r) * L + tb + t0;
+          pf_dt[k] = *(const RawV*)((const S*)p.delta + base);
+          pf_u[k] = *(const RawV*)((const S*)p.u + base);
+          if (MODE == 0) pf_z[k] = *(const RawV*)((const S*)p.zsrc + base);
+        } else {
+          const bool rok = c < NCHUNK && r < rows_in;
+          const int64_t base = ((int64_t)b * p.dim + d_base + r) * L + tb + t0;
+          RawV rd = {}, ru = {}, rz = {};
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) {
+            if (rok && t0 + q < nvalid) {
+              IO::template pack_elem<VEC>(rd, q, IO::ld_bits(p.delta, base + q));
+              IO::template pack_elem<VEC>(ru, q, IO::ld_bits(p.u, base + q));
+              if (MODE == 0) IO::template pack_elem<VEC>(rz, q, IO::ld_bits(p.zsrc, base + q));
+            }
+          }
+          pf_dt[k] = rd; pf_u[k] = ru; pf_z[k] = rz;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int t = w + k * NW;
+        const int64_t tt = tb + ((t < nvalid) ? t : 0);        // clamped to a valid step
+        const int pp = r0 + (row_ok ? lane : 0);                // clamped to a valid position
+        pm_dt[k] = IO::ld_bits(p.delta, ((int64_t)b * L + tt) * p.H + hh);
+        const int64_t xi = (((int64_t)b * L + tt) * p.H + hh) * p.P + pp;
+        pm_u[k] = IO::ld_bits(p.u, xi);
+        if (MODE == 0) pm_z[k] = IO::ld_bits(p.zsrc, xi);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NBC; ++k) {
+      const int i = tid + k * NT;
+      const int which = i / (NPAD * TB), rem = i % (NPAD * TB);
+      int n, t;
+      if (LAYOUT == 0) { n = rem / TB; t = rem % TB; } else { t = rem / NPAD; n = rem % NPAD; }
+      if (!(i < NBCV && n < p.N && t < nvalid)) { n = 0; t = 0; }   // clamped, masked in phase A
+      const int64_t bi = (LAYOUT == 0) ? (((int64_t)b * p.G + g) * p.N + n) * L + tb + t
+                                       : (((int64_t)b * L + tb + t) * p.G + g) * p.N + n;
+      pf_bc[k] = IO::ld_bits(which == 0 ? p.B : p.C, bi);
+    }
+  };
+
+  // per-row constants of the chunks this thread owns in phases A and C (loaded once)
+  float c_bias[LAYOUT == 0 ? CPT : 1], c_D[LAYOUT == 0 ? CPT : 1];
+  if (LAYOUT == 0) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = tid + k * NT;
+      const int r = c / CH_PER_ROW;
+      const bool rok = c < NCHUNK && r < rows_in;
+      c_bias[k] = (p.bias && rok) ? p.bias[d_base + r] : 0.0f;
+      c_D[k] = (p.D && rok) ? p.D[d_base + r] : 0.0f;
+    }
+  }
   const float bias_head = (LAYOUT == 1 && p.bias) ? p.bias[hh] : 0.0f;
+  const float D_lane = (LAYOUT == 1 && p.D && row_ok) ? p.D[d] : 0.0f;
+
+  if (t_seg0 < t_seg1) issue_loads(t_seg0);
+  // Everything loaded so far (state, constants) is complete before the loop, so the
+  // only loads in flight inside it are the block prefetches.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   for (int64_t t_blk = t_seg0; t_blk < t_seg1; t_blk += TB) {
     const int nvalid = (int)min((int64_t)TB, t_seg1 - t_blk);
@@ -186,72 +316,47 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
         const int c = tid + k * NT;
         if (c < NCHUNK) {
           const int r = c / CH_PER_ROW;
-          const int t4 = (c % CH_PER_ROW) * 4;
-          const int dd = d_base + r;
+          const int t0 = (c % CH_PER_ROW) * VEC;
           const bool rok = r < rows_in;
-          const float br = (p.bias && rok) ? p.bias[dd] : 0.0f;
-          const int64_t base = ((int64_t)b * p.dim + dd) * L + t_blk + t4;
-          float raw[4], uu[4], zz[4];
-          if (rok && p.vec_ok && t4 + 4 <= nvalid) {
-            IO::ld4(p.delta, base, raw);
-            IO::ld4(p.u, base, uu);
-            if (MODE == 0 && p.z) IO::ld4(p.z, base, zz);
-          } else {
+          const float br = c_bias[k];
+          float raw[VEC], uu[VEC], zz[VEC];
+          IO::template unpack<VEC>(pf_dt[k], raw);
+          IO::template unpack<VEC>(pf_u[k], uu);
+          IO::template unpack<VEC>(pf_z[k], zz);
+          float dtv[VEC], duv[VEC];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const bool ok = rok && t4 + q < nvalid;
-              raw[q] = ok ? IO::ld(p.delta, base + q) : 0.0f;
-              uu[q] = ok ? IO::ld(p.u, base + q) : 0.0f;
-              zz[q] = (MODE == 0 && p.z && ok) ? IO::ld(p.z, base + q) : 0.0f;
-            }
-          }
-          float dtv[4], duv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bool ok = rok && t4 + q < nvalid;
+          for (int q = 0; q < VEC; ++q) {
+            const bool ok = rok && t0 + q < nvalid;
             const float rr = raw[q] + br;
-            float dt = p.softplus ? softplus_f(rr) : rr;
-            dt = ok ? dt : 0.0f;
+            const float dt = ok ? (p.softplus ? softplus_f(rr) : rr) : 0.0f;
             dtv[q] = dt;
             duv[q] = dt * uu[q];
-            keep_u[k * 4 + q] = uu[q];
-            keep_z[k * 4 + q] = (MODE == 0 && p.z) ? zz[q] : 0.0f;
+            keep_u[k * VEC + q] = uu[q];
+            keep_z[k * VEC + q] = zz[q];
           }
-          *(float4*)&s_dt[r * TP + t4] = make_float4(dtv[0], dtv[1], dtv[2], dtv[3]);
-          *(float4*)&s_du[r * TP + t4] = make_float4(duv[0], duv[1], duv[2], duv[3]);
+          if constexpr (VEC == 4) {
+            *(float4*)&s_dt[r * TP + t0] = make_float4(dtv[0], dtv[1], dtv[2], dtv[3]);
+            *(float4*)&s_du[r * TP + t0] = make_float4(duv[0], duv[1], duv[2], duv[3]);
+          } else if constexpr (VEC == 2) {
+            *(float2*)&s_dt[r * TP + t0] = make_float2(dtv[0], dtv[1]);
+            *(float2*)&s_du[r * TP + t0] = make_float2(duv[0], duv[1]);
+          } else {
+            s_dt[r * TP + t0] = dtv[0];
+            s_du[r * TP + t0] = duv[0];
+          }
         }
-      }
-      // B_t, C_t of the block: B/C are (B, G, N, L)
-      for (int i = tid; i < NPAD * TB; i += NT) {
-        const int n = i / TB, t = i % TB;
-        float bv = 0.0f, cv = 0.0f;
-        if (n < p.N && t < nvalid) {
-          const int64_t bi = (((int64_t)b * p.G + g) * p.N + n) * L + t_blk + t;
-          bv = IO::ld(p.B, bi);
-          if (MODE == 0) cv = IO::ld(p.C, bi);
-        }
-        const int ww = n / NS, j = n % NS;
-        s_bc[(t * NW + ww) * 2 * NS + j] = bv;
-        s_bc[(t * NW + ww) * 2 * NS + NS + j] = cv;
       }
     } else {
-      // BLHP: thread (lane = position, tq) handles steps tq, tq + NW, ...
-      const int tq = w;
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
-        const int t = tq + k * NW;
+        const int t = w + k * NW;
         if (t < TB) {
           const bool tok = t < nvalid;
-          const int64_t tt = t_blk + t;
-          float raw = tok ? IO::ld(p.delta, ((int64_t)b * L + tt) * p.H + hh) : 0.0f;
-          const float rr = raw + bias_head;
-          float dt = p.softplus ? softplus_f(rr) : rr;
-          dt = tok ? dt : 0.0f;
-          const int64_t xi = (((int64_t)b * L + tt) * p.H + hh) * p.P + r0 + lane;
-          const bool ok = tok && row_ok;
-          const float uu = ok ? IO::ld(p.u, xi) : 0.0f;
+          const float rr = IO::cvt(pm_dt[k]) + bias_head;
+          const float dt = tok ? (p.softplus ? softplus_f(rr) : rr) : 0.0f;
+          const float uu = IO::cvt(pm_u[k]);
           keep_u[k] = uu;
-          keep_z[k] = (MODE == 0 && p.z && ok) ? IO::ld(p.z, xi) : 0.0f;
+          keep_z[k] = IO::cvt(pm_z[k]);
           s_du[t * 65 + lane] = dt * uu;
           if (lane == 0) {
             s_dt[t] = dt;
@@ -259,23 +364,25 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
           }
         }
       }
-      // B_t, C_t: (B, L, G, N)
-      for (int i = tid; i < NPAD * TB; i += NT) {
-        const int t = i / NPAD, n = i % NPAD;
-        float bv = 0.0f, cv = 0.0f;
-        if (n < p.N && t < nvalid) {
-          const int64_t bi = (((int64_t)b * L + t_blk + t) * p.G + g) * p.N + n;
-          bv = IO::ld(p.B, bi);
-          if (MODE == 0) cv = IO::ld(p.C, bi);
-        }
-        const int ww = n / NS, j = n % NS;
-        s_bc[(t * NW + ww) * 2 * NS + j] = bv;
-        s_bc[(t * NW + ww) * 2 * NS + NS + j] = cv;
+    }
+#pragma unroll
+    for (int k = 0; k < NBC; ++k) {
+      const int i = tid + k * NT;
+      if (i < NBCV) {
+        const int which = i / (NPAD * TB), rem = i % (NPAD * TB);
+        int n, t;
+        if (LAYOUT == 0) { n = rem / TB; t = rem % TB; } else { t = rem / NPAD; n = rem % NPAD; }
+        const bool ok = n < p.N && t < nvalid;
+        s_bc[(t * NW + n / NS) * 2 * NS + which * NS + n % NS] = ok ? IO::cvt(pf_bc[k]) : 0.0f;
       }
     }
     __syncthreads();
 
+    // prefetch the next block while this one is scanned
+    if (t_blk + TB < t_seg1) issue_loads(t_blk + TB);
+
     // =========================== phase B ===========================
+#pragma unroll
     for (int t4 = 0; t4 < TB; t4 += 4) {
       float dtq[4], duq[4], yq[4];
       if (LAYOUT == 0) {
@@ -290,38 +397,43 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
           duq[q] = s_du[(t4 + q) * 65 + lane];
         }
       }
+      // B_t, C_t of this wave's states (2*NS floats per step), read QB steps ahead of the math
+      constexpr int NREAD = (MODE == 0 ? 2 * NS : NS);
+      constexpr int QB = (2 * NS <= 4) ? 4 : (2 * NS <= 8) ? 2 : 1;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int t = t4 + q;
-        // B_t[w*NS .. +NS) then C_t[...] for this wave: 2*NS floats, 16-byte aligned
-        float bcv[2 * NS];
-        const float* bc = &s_bc[(t * NW + w) * 2 * NS];
-        constexpr int NREAD = (MODE == 0 ? 2 * NS : NS);
-        if constexpr (NREAD % 4 == 0) {
+      for (int q0 = 0; q0 < 4; q0 += QB) {
+        float bcv[QB][2 * NS];
 #pragma unroll
-          for (int j = 0; j < NREAD; j += 4) {
-            const float4 v = *(const float4*)&bc[j];
-            bcv[j] = v.x; bcv[j + 1] = v.y; bcv[j + 2] = v.z; bcv[j + 3] = v.w;
-          }
-        } else {
+        for (int qq = 0; qq < QB; ++qq) {
+          const float* bc = &s_bc[((t4 + q0 + qq) * NW + w) * 2 * NS];
+          if constexpr (NREAD % 4 == 0) {
 #pragma unroll
-          for (int j = 0; j < NREAD; j += 2) {
-            const float2 v = *(const float2*)&bc[j];
-            bcv[j] = v.x; bcv[j + 1] = v.y;
+            for (int j = 0; j < NREAD; j += 4) {
+              const float4 v = *(const float4*)&bc[j];
+              bcv[qq][j] = v.x; bcv[qq][j + 1] = v.y; bcv[qq][j + 2] = v.z; bcv[qq][j + 3] = v.w;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NREAD; j += 2) {
+              const float2 v = *(const float2*)&bc[j];
+              bcv[qq][j] = v.x; bcv[qq][j + 1] = v.y;
+            }
           }
         }
-        const float* Bv = bcv;
-        const float* Cv = bcv + NS;
-        const float a_head = (LAYOUT == 1) ? s_a[t] : 0.0f;
-        float acc = 0.0f;
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          const float a = (LAYOUT == 0) ? __builtin_amdgcn_exp2f(dtq[q] * A2[j]) : a_head;
-          h[j] = fmaf(a, h[j], duq[q] * Bv[j]);
-          if (MODE == 0) acc = fmaf(Cv[j], h[j], acc);
+        for (int qq = 0; qq < QB; ++qq) {
+          const int q = q0 + qq;
+          const float a_head = (LAYOUT == 1) ? s_a[t4 + q] : 0.0f;
+          float acc = 0.0f;
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            const float a = (LAYOUT == 0) ? __builtin_amdgcn_exp2f(dtq[q] * A2[j]) : a_head;
+            h[j] = fmaf(a, h[j], duq[q] * bcv[qq][j]);
+            if (MODE == 0) acc = fmaf(bcv[qq][NS + j], h[j], acc);
+          }
+          yq[q] = acc;
+          if (MODE == 1) sum_dt += dtq[q];
         }
-        yq[q] = acc;
-        if (MODE == 1) sum_dt += dtq[q];
       }
       if (MODE == 0) {
         if (LAYOUT == 0) {
@@ -342,45 +454,54 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
           const int c = tid + k * NT;
           if (c < NCHUNK) {
             const int r = c / CH_PER_ROW;
-            const int t4 = (c % CH_PER_ROW) * 4;
+            const int t0 = (c % CH_PER_ROW) * VEC;
             const int dd = d_base + r;
             if (r < rows_in) {
-              float ys[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+              float ys[VEC];
+#pragma unroll
+              for (int q = 0; q < VEC; ++q) ys[q] = 0.0f;
 #pragma unroll
               for (int ww = 0; ww < NW; ++ww) {
-                const float4 v = *(const float4*)&s_yp[(ww * 64 + r) * TP + t4];
-                ys[0] += v.x; ys[1] += v.y; ys[2] += v.z; ys[3] += v.w;
+                const float* src = &s_yp[(ww * 64 + r) * TP + t0];
+                if constexpr (VEC == 4) {
+                  const float4 v = *(const float4*)src;
+                  ys[0] += v.x; ys[1] += v.y; ys[2] += v.z; ys[3] += v.w;
+                } else if constexpr (VEC == 2) {
+                  const float2 v = *(const float2*)src;
+                  ys[0] += v.x; ys[1] += v.y;
+                } else {
+                  ys[0] += src[0];
+                }
               }
-              const float Dd = p.D ? p.D[dd] : 0.0f;
+              const float Dd = c_D[k];
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float yv = fmaf(Dd, keep_u[k * 4 + q], ys[q]);
-                if (p.z) yv *= silu_f(keep_z[k * 4 + q]);
+              for (int q = 0; q < VEC; ++q) {
+                float yv = fmaf(Dd, keep_u[k * VEC + q], ys[q]);
+                if (p.has_z) yv *= silu_f(keep_z[k * VEC + q]);
                 ys[q] = yv;
               }
-              const int64_t base = ((int64_t)b * p.dim + dd) * L + t_blk + t4;
-              if (p.vec_ok && t4 + 4 <= nvalid) {
-                IO::st4(p.y, base, ys);
+              const int64_t base = ((int64_t)b * p.dim + dd) * L + t_blk + t0;
+              if (vec_ok && t0 + VEC <= nvalid) {
+                IO::template stv<VEC>(p.y, base, ys);
               } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                  if (t4 + q < nvalid) IO::st(p.y, base + q, ys[q]);
+                for (int q = 0; q < VEC; ++q)
+                  if (t0 + q < nvalid) IO::st(p.y, base + q, ys[q]);
               }
             }
           }
         }
       } else {
-        const int tq = w;
-        const float Dd = (p.D && row_ok) ? p.D[d] : 0.0f;
+        const float Dd = D_lane;
 #pragma unroll
         for (int k = 0; k < TPT; ++k) {
-          const int t = tq + k * NW;
+          const int t = w + k * NW;
           if (t < nvalid && row_ok) {
             float ys = 0.0f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) ys += s_yp[(ww * TB + t) * 65 + lane];
             float yv = fmaf(Dd, keep_u[k], ys);
-            if (p.z) yv *= silu_f(keep_z[k]);
+            if (p.has_z) yv *= silu_f(keep_z[k]);
             const int64_t xi = (((int64_t)b * L + t_blk + t) * p.H + hh) * p.P + r0 + lane;
             IO::st(p.y, xi, yv);
           }
@@ -415,23 +536,307 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
   }
 }
 
+// ------------------------------------------------- row-group kernel ((B,D,L), N <= 32)
+// One wave owns 8 rows (channels of one batch item and channel group) and their
+// whole state vector: 8 lanes per row, NS states per lane.  Waves never wait for
+// each other: there is no workgroup barrier.  A time block is 32 steps; lane k of a
+// row loads, prepares (step size, dt*u) and finishes (readout sum, D*u, gate, store)
+// steps 4k..4k+3 of its row, and shares the prepared values with the other lanes of
+// the row through a per-wave LDS tile.  B_t/C_t of the block are staged per wave in
+// LDS.  The readout partial sums of the 8 lanes of a row are combined through LDS.
+// Full blocks use vector loads issued one block ahead; the ragged last block of a
+// segment is loaded element by element after the main loop.
+namespace rg {
+constexpr int LPR = 8;          // lanes per row
+constexpr int RPW = 64 / LPR;   // rows per wave
+constexpr int TB = 4 * LPR;     // steps per block (4 per lane)
+constexpr int TP = TB + 4;      // padded LDS row stride
+constexpr int WPG = 4;          // waves per workgroup (independent; packing only)
+}  // namespace rg
+
+// order the wave's own LDS writes before its reads of other lanes' data
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename IO, int NS, int MODE, bool VECOK>
+__global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
+  using namespace rg;
+  using S = typename IO::S;
+  constexpr int NPAD = LPR * NS;
+  constexpr int SV = NPAD * TB / 64;                         // B (and C) values staged per lane
+  constexpr int NQ = SV * IO::kBytes / 16;                   // 16-byte loads per lane per tensor
+  static_assert(NQ >= 1 && (SV * IO::kBytes) % 16 == 0, "staging width");
+  using Raw4 = typename RawT<4 * IO::kBytes>::T;             // 4 steps of one tensor
+  constexpr int TILE = (RPW * LPR * TP > 2 * RPW * TP) ? RPW * LPR * TP : 2 * RPW * TP;
+
+  __shared__ __attribute__((aligned(16))) float s_tile[WPG][TILE];        // dt|du, later partial sums
+  __shared__ __attribute__((aligned(16))) float s_bc[WPG][TB * 2 * NPAD];  // [t][k][B(NS) C(NS)]
+
+  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row = lane / LPR, k = lane % LPR;
+  const int rb = blockIdx.x * WPG + wv;
+  if (rb >= p.blocks_per_group * p.G) return;               // no barriers: idle waves may leave
+  float* const s_dt = &s_tile[wv][0];
+  float* const s_du = &s_tile[wv][RPW * TP];
+  float* const s_part = &s_tile[wv][0];
+  float* const s_b = &s_bc[wv][0];
+
+  const int b = blockIdx.y;
+  const int seg = blockIdx.z;
+  const int64_t L = p.L;
+  const int64_t t_seg0 = (int64_t)seg * p.seg_len;
+  const int64_t t_seg1 = min(L, t_seg0 + p.seg_len);
+  const int g = rb / p.blocks_per_group;
+  const int r0 = (rb % p.blocks_per_group) * RPW;
+  const int rows_in = min(RPW, p.rows_per_group - r0);
+  const bool row_ok = row < rows_in;
+  const int d = g * p.rows_per_group + r0 + (row_ok ? row : 0);   // clamped to a valid channel
+
+  // ---- states n = k*NS + j of channel d
+  float h[NS], A2[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int n = k * NS + j;
+    const bool ok = row_ok && n < p.N;
+    h[j] = (MODE == 0 && ok && p.h0) ? p.h0[((int64_t)b * p.dim + d) * p.N + n] : 0.0f;
+    A2[j] = ok ? p.A[(int64_t)d * p.N + n] * kLog2e : 0.0f;
+  }
+  if (MODE == 0 && seg > 0 && row_ok) {
+    for (int s2 = 0; s2 < seg; ++s2) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int64_t i = (((int64_t)s2 * p.batch + b) * p.Npad + k * NS + j) * p.dim + d;
+        h[j] = fmaf(p.wsP[i], h[j], p.wsH[i]);
+      }
+    }
+  }
+  const float bias = (p.bias && row_ok) ? p.bias[d] : 0.0f;
+  const float Dd = (p.D && row_ok) ? p.D[d] : 0.0f;
+  float sum_dt = 0.0f;
+
+  const int64_t xrow = ((int64_t)b * p.dim + d) * L;          // start of this row in u/delta/z/y
+  const int n_s = lane / (TB / SV);                           // staging: state and first step
+  const int t_s = (lane % (TB / SV)) * SV;
+  const int n_sc = n_s < p.N ? n_s : 0;                       // clamped state for loads
+  const int64_t brow = (((int64_t)b * p.G + g) * p.N + n_sc) * L;   // B/C row of that state
+
+  // --------------------------------------------------------- one time block
+  // xin: delta/u/z of steps 4k..4k+3 (fp32); bcin: staged B then C values; nvalid steps
+  auto run_block = [&](int64_t tb, int nvalid, const float* raw, const float* uu, const float* zz,
+                       const float* bv, const float* cv) {
+    // prologue: step sizes and dt*u of this lane's 4 steps
+    float dtv[4], duv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = 4 * k + q < nvalid;
+      const float rr = raw[q] + bias;
+      const float dt = ok ? (p.softplus ? softplus_f(rr) : rr) : 0.0f;
+      dtv[q] = dt;
+      duv[q] = dt * uu[q];
+    }
+    *(float4*)&s_dt[row * TP + 4 * k] = make_float4(dtv[0], dtv[1], dtv[2], dtv[3]);
+    *(float4*)&s_du[row * TP + 4 * k] = make_float4(duv[0], duv[1], duv[2], duv[3]);
+    // staged B/C of state n_s, steps t_s .. t_s+SV-1 (zero beyond N or past the block)
+#pragma unroll
+    for (int i = 0; i < SV; ++i) {
+      const bool ok = n_s < p.N && t_s + i < nvalid;
+      float* dst = &s_b[(t_s + i) * 2 * NPAD + (n_s / NS) * 2 * NS + n_s % NS];
+      dst[0] = ok ? bv[i] : 0.0f;
+      if (MODE == 0) dst[NS] = ok ? cv[i] : 0.0f;
+    }
+    wave_lds_sync();
+
+    // the recurrence over the 32 steps for this lane's NS states
+    float part[MODE == 0 ? TB : 1];
+#pragma unroll
+    for (int t4 = 0; t4 < TB; t4 += 4) {
+      const float4 a4 = *(const float4*)&s_dt[row * TP + t4];
+      const float4 b4 = *(const float4*)&s_du[row * TP + t4];
+      const float dtq[4] = {a4.x, a4.y, a4.z, a4.w};
+      const float duq[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float* bc = &s_b[(t4 + q) * 2 * NPAD + k * 2 * NS];
+        float Bv[NS], Cv[NS];
+#pragma unroll
+        for (int j = 0; j < NS; j += 2) {
+          const float2 v = *(const float2*)&bc[j];
+          Bv[j] = v.x; Bv[j + 1] = v.y;
+          if (MODE == 0) {
+            const float2 c = *(const float2*)&bc[NS + j];
+            Cv[j] = c.x; Cv[j + 1] = c.y;
+          }
+        }
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const float a = __builtin_amdgcn_exp2f(dtq[q] * A2[j]);
+          h[j] = fmaf(a, h[j], duq[q] * Bv[j]);
+          if (MODE == 0) acc = fmaf(Cv[j], h[j], acc);
+        }
+        if (MODE == 0) part[t4 + q] = acc;
+        if (MODE == 1) sum_dt += dtq[q];
+      }
+    }
+    if (MODE == 0) {
+      wave_lds_sync();   // all lanes are done reading dt/du (the partial tile aliases them)
+#pragma unroll
+      for (int t4 = 0; t4 < TB; t4 += 4)
+        *(float4*)&s_part[(row * LPR + k) * TP + t4] =
+            make_float4(part[t4], part[t4 + 1], part[t4 + 2], part[t4 + 3]);
+      wave_lds_sync();
+      float ys[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < LPR; ++kk) {
+        const float4 v = *(const float4*)&s_part[(row * LPR + kk) * TP + 4 * k];
+        ys[0] += v.x; ys[1] += v.y; ys[2] += v.z; ys[3] += v.w;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float yv = fmaf(Dd, uu[q], ys[q]);
+        if (p.has_z) yv *= silu_f(zz[q]);
+        ys[q] = yv;
+      }
+      if (row_ok) {
+        if (VECOK && nvalid == TB) {
+          IO::template stv<4>(p.y, xrow + tb + 4 * k, ys);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (4 * k + q < nvalid) IO::st(p.y, xrow + tb + 4 * k + q, ys[q]);
+        }
+      }
+    }
+    wave_lds_sync();     // the next block rewrites the tiles this one read
+  };
+
+  // ------------------------------------------------- full blocks, prefetched
+  int64_t t_blk = t_seg0;
+  if (VECOK) {
+    const int64_t n_full = (t_seg1 - t_seg0) / TB;
+    Raw4 pf_dt, pf_u, pf_z;
+    uint4 pf_b[NQ], pf_c[NQ];
+    auto issue = [&](int64_t tb) {
+      pf_dt = *(const Raw4*)((const S*)p.delta + xrow + tb + 4 * k);
+      pf_u = *(const Raw4*)((const S*)p.u + xrow + tb + 4 * k);
+      if (MODE == 0) pf_z = *(const Raw4*)((const S*)p.zsrc + xrow + tb + 4 * k);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        pf_b[i] = *(const uint4*)((const S*)p.B + brow + tb + t_s + i * (16 / IO::kBytes));
+        if (MODE == 0) pf_c[i] = *(const uint4*)((const S*)p.C + brow + tb + t_s + i * (16 / IO::kBytes));
+      }
+    };
+    if (n_full > 0) issue(t_blk);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): only prefetches are in flight inside the loop
+    for (int64_t it = 0; it < n_full; ++it, t_blk += TB) {
+      float raw[4], uu[4], zz[4], bv[SV], cv[SV];
+      IO::template unpack<4>(pf_dt, raw);
+      IO::template unpack<4>(pf_u, uu);
+      IO::template unpack<4>(pf_z, zz);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        constexpr int E = 16 / IO::kBytes;
+        IO::template unpack<E>(*(const typename RawT<16>::T*)&pf_b[i], &bv[i * E]);
+        if (MODE == 0) IO::template unpack<E>(*(const typename RawT<16>::T*)&pf_c[i], &cv[i * E]);
+      }
+      if (it + 1 < n_full) issue(t_blk + TB);
+      run_block(t_blk, TB, raw, uu, zz, bv, cv);
+    }
+  }
+  // ------------------------------------------ remaining steps, element loads
+  for (; t_blk < t_seg1; t_blk += TB) {
+    const int nvalid = (int)min((int64_t)TB, t_seg1 - t_blk);
+    float raw[4], uu[4], zz[4], bv[SV], cv[SV];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = 4 * k + q < nvalid;
+      const int64_t i = xrow + t_blk + (ok ? 4 * k + q : 0);
+      raw[q] = IO::cvt(IO::ld_bits(p.delta, i));
+      uu[q] = IO::cvt(IO::ld_bits(p.u, i));
+      zz[q] = (MODE == 0) ? IO::cvt(IO::ld_bits(p.zsrc, i)) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < SV; ++i) {
+      const bool ok = t_s + i < nvalid;
+      const int64_t bi = brow + t_blk + (ok ? t_s + i : 0);
+      bv[i] = IO::cvt(IO::ld_bits(p.B, bi));
+      cv[i] = (MODE == 0) ? IO::cvt(IO::ld_bits(p.C, bi)) : 0.0f;
+    }
+    run_block(t_blk, nvalid, raw, uu, zz, bv, cv);
+  }
+
+  // ---- outputs of the pass
+  if (MODE == 1) {
+    if (row_ok) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int64_t i = (((int64_t)seg * p.batch + b) * p.Npad + k * NS + j) * p.dim + d;
+        p.wsP[i] = __builtin_amdgcn_exp2f(sum_dt * A2[j]);
+        p.wsH[i] = h[j];
+      }
+    }
+  } else if (p.h_last && row_ok && seg == p.nseg - 1) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int n = k * NS + j;
+      if (n < p.N) p.h_last[((int64_t)b * p.dim + d) * p.N + n] = h[j];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launchers
-template <int LAYOUT, typename IO, int NS, int NW, int TB>
-int launch_variant(const Plan& pl, const KParams& kp, hipStream_t st) {
+template <int LAYOUT, typename IO, int NS, int NW, int TB, bool VECOK>
+int launch_modes(const Plan& pl, const KParams& kp, hipStream_t st) {
   const dim3 block(NW * 64);
   if (pl.nseg > 1) {
     const dim3 grid_agg(pl.grid_rows, kp.batch, pl.nseg - 1);
-    hipLaunchKernelGGL((scan_kernel<LAYOUT, IO, NS, NW, TB, 1>), grid_agg, block, 0, st, kp);
+    hipLaunchKernelGGL((scan_kernel<LAYOUT, IO, NS, NW, TB, 1, VECOK>), grid_agg, block, 0, st, kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
   const dim3 grid(pl.grid_rows, kp.batch, pl.nseg);
-  hipLaunchKernelGGL((scan_kernel<LAYOUT, IO, NS, NW, TB, 0>), grid, block, 0, st, kp);
+  hipLaunchKernelGGL((scan_kernel<LAYOUT, IO, NS, NW, TB, 0, VECOK>), grid, block, 0, st, kp);
   return (int)hipGetLastError();
+}
+
+template <int LAYOUT, typename IO, int NS, int NW, int TB>
+int launch_variant(const Plan& pl, const KParams& kp, hipStream_t st) {
+  constexpr int VEC = chunk_width<NW * 64, TB>();
+  if (LAYOUT == 1 || kp.L % VEC == 0) return launch_modes<LAYOUT, IO, NS, NW, TB, true>(pl, kp, st);
+  return launch_modes<LAYOUT, IO, NS, NW, TB, false>(pl, kp, st);
+}
+
+template <typename IO, int NS, bool VECOK>
+int launch_rowgroup_modes(const Plan& pl, const KParams& kp, hipStream_t st) {
+  const dim3 block(rg::WPG * 64);
+  const int total = kp.blocks_per_group * kp.G;
+  const int gx = (total + rg::WPG - 1) / rg::WPG;
+  if (pl.nseg > 1) {
+    hipLaunchKernelGGL((rowgroup_kernel<IO, NS, 1, VECOK>), dim3(gx, kp.batch, pl.nseg - 1), block, 0, st, kp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  hipLaunchKernelGGL((rowgroup_kernel<IO, NS, 0, VECOK>), dim3(gx, kp.batch, pl.nseg), block, 0, st, kp);
+  return (int)hipGetLastError();
+}
+
+template <typename IO, int NS>
+int launch_rowgroup(const Plan& pl, const KParams& kp, hipStream_t st) {
+  if (kp.L % 8 == 0) return launch_rowgroup_modes<IO, NS, true>(pl, kp, st);
+  return launch_rowgroup_modes<IO, NS, false>(pl, kp, st);
 }
 
 template <int LAYOUT, typename IO>
 int launch_io(const Plan& pl, const KParams& kp, hipStream_t st) {
+  if (LAYOUT == 0 && pl.kernel == 1) {
+    if (pl.Npad == 16) return launch_rowgroup<IO, 2>(pl, kp, st);
+    if (pl.Npad == 32) return launch_rowgroup<IO, 4>(pl, kp, st);
+    return (int)hipErrorInvalidValue;
+  }
   // (NS, NW, TB) per padded state count; the plan's TB must match (make_plan).
   switch (pl.Npad) {
     case 16: return launch_variant<LAYOUT, IO, 2, 8, 16>(pl, kp, st);

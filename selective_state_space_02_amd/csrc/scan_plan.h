@@ -16,12 +16,13 @@
 namespace ssm {
 
 struct Plan {
+  int kernel = 0;            // 0: workgroup kernel (64 rows, states over waves); 1: row-group kernel
   int layout = 0, io = 0;
   int NS = 0, NW = 0, TB = 0, Npad = 0;
   int nseg = 1;
   int64_t seg_len = 0;
-  int blocks_per_group = 0;  // row blocks of 64 per channel group (BDL) or per head (BLHP)
-  int grid_rows = 0;         // row blocks per batch item
+  int blocks_per_group = 0;  // row blocks per channel group (BDL) or per head (BLHP)
+  int grid_rows = 0;         // workgroups per batch item and segment
   bool vec_ok = false;       // 4-step vector loads allowed along time (BDL)
   size_t ws_bytes = 0;
 };
@@ -34,6 +35,7 @@ struct KParams {
   const void* C;
   const float* D;
   const void* z;
+  const void* zsrc;     // z, or u when there is no gate (prefetched unconditionally, unused then)
   const float* bias;
   const float* h0;
   void* y;
@@ -43,9 +45,10 @@ struct KParams {
   int64_t L, seg_len;
   int batch, dim, N, Npad, H, P, G;
   int rows_per_group;    // BDL: dim / G;  BLHP: P
-  int blocks_per_group;  // ceil(rows_per_group / 64)
+  int blocks_per_group;  // row blocks per group / head (64 rows, or 8 for the row-group kernel)
   int heads_per_group;   // BLHP: H / G
   int softplus;
+  int has_z;
   int vec_ok;
   int nseg;
 };

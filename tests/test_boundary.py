@@ -121,13 +121,12 @@ def test_workspace_too_small():
 def test_workspace_size_and_plan():
     d = dims(batch=4, seqlen=2048, dim=5120, dstate=16)               # 320 row blocks: no segments
     assert scan.workspace_size(d) == 0
-    assert "nseg" not in scan.describe(d) or True
     txt = scan.describe(d)
-    assert "layout=bdl" in txt and "NS=2" in txt and "NW=8" in txt
+    assert "kernel=rowgroup" in txt and "layout=bdl" in txt and "NS=2" in txt
     d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # 40 row blocks: segmented
     assert scan.workspace_size(d4) > 0
     d5 = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
-    assert "NS=16" in scan.describe(d5)
+    assert "kernel=workgroup" in scan.describe(d5) and "NS=16" in scan.describe(d5)
     bad = dims(dim=0)
     assert scan.workspace_size(bad) == 0
     with pytest.raises(ValueError):
