@@ -650,36 +650,77 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
     }
     wave_lds_sync();
 
-    // the recurrence over the 32 steps for this lane's NS states
+    // The recurrence over the 32 steps for this lane's NS states.  Software
+    // pipelined by groups of 4 steps: the LDS operands of group g+1 are read while
+    // group g computes, and a group's decay factors (independent of the state) are
+    // all formed before its recurrence, so LDS and transcendental latencies overlap
+    // with arithmetic instead of stalling the wave.
+    constexpr int NBC = (MODE == 0 ? 2 : 1) * NS;            // B (and C) floats per step
     float part[MODE == 0 ? TB : 1];
-#pragma unroll
-    for (int t4 = 0; t4 < TB; t4 += 4) {
-      const float4 a4 = *(const float4*)&s_dt[row * TP + t4];
-      const float4 b4 = *(const float4*)&s_du[row * TP + t4];
-      const float dtq[4] = {a4.x, a4.y, a4.z, a4.w};
-      const float duq[4] = {b4.x, b4.y, b4.z, b4.w};
+    float4 cur_dt, cur_du, nxt_dt, nxt_du;
+    float cur_bc[4][NBC], nxt_bc[4][NBC];
+    auto load_group = [&](int t4, float4& dt4, float4& du4, float (&bc)[4][NBC]) {
+      dt4 = *(const float4*)&s_dt[row * TP + t4];
+      du4 = *(const float4*)&s_du[row * TP + t4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float* bc = &s_b[(t4 + q) * 2 * NPAD + k * 2 * NS];
-        float Bv[NS], Cv[NS];
+        const float* src = &s_b[(t4 + q) * 2 * NPAD + k * 2 * NS];
 #pragma unroll
-        for (int j = 0; j < NS; j += 2) {
-          const float2 v = *(const float2*)&bc[j];
-          Bv[j] = v.x; Bv[j + 1] = v.y;
-          if (MODE == 0) {
-            const float2 c = *(const float2*)&bc[NS + j];
-            Cv[j] = c.x; Cv[j + 1] = c.y;
-          }
+        for (int j = 0; j < NBC; j += 2) {
+          const float2 v = *(const float2*)&src[j];
+          bc[q][j] = v.x; bc[q][j + 1] = v.y;
         }
+      }
+    };
+    // decay factors and inputs of one group, formed one group ahead of their use
+    float ca[4][NS], cbx[4][NS], cC[4][NS], csd[4];
+    auto prep_group = [&](const float4& dt4, const float4& du4, const float (&bc)[4][NBC]) {
+      const float dtq[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
+      const float duq[4] = {du4.x, du4.y, du4.z, du4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        csd[q] = dtq[q];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          ca[q][j] = __builtin_amdgcn_exp2f(dtq[q] * A2[j]);
+          cbx[q][j] = duq[q] * bc[q][j];
+          if (MODE == 0) cC[q][j] = bc[q][NS + j];
+        }
+      }
+    };
+    load_group(0, cur_dt, cur_du, cur_bc);
+    load_group(4, nxt_dt, nxt_du, nxt_bc);
+    prep_group(cur_dt, cur_du, cur_bc);
+#pragma unroll
+    for (int t4 = 0; t4 < TB; t4 += 4) {
+      // operands of this group, then start the next group's loads and decays
+      float a[4][NS], bx[4][NS], Cc[4][NS], sd[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sd[q] = csd[q];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) { a[q][j] = ca[q][j]; bx[q][j] = cbx[q][j]; Cc[q][j] = cC[q][j]; }
+      }
+      if (t4 + 4 < TB) {
+        cur_dt = nxt_dt;
+        cur_du = nxt_du;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < NBC; ++j) cur_bc[q][j] = nxt_bc[q][j];
+        if (t4 + 8 < TB) load_group(t4 + 8, nxt_dt, nxt_du, nxt_bc);
+        prep_group(cur_dt, cur_du, cur_bc);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          const float a = __builtin_amdgcn_exp2f(dtq[q] * A2[j]);
-          h[j] = fmaf(a, h[j], duq[q] * Bv[j]);
-          if (MODE == 0) acc = fmaf(Cv[j], h[j], acc);
+          h[j] = fmaf(a[q][j], h[j], bx[q][j]);
+          if (MODE == 0) acc = fmaf(Cc[q][j], h[j], acc);
         }
         if (MODE == 0) part[t4 + q] = acc;
-        if (MODE == 1) sum_dt += dtq[q];
+        if (MODE == 1) sum_dt += sd[q];
       }
     }
     if (MODE == 0) {
