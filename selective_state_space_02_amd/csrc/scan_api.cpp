@@ -94,7 +94,8 @@ int make_plan(const ssm_dims_t* d, Plan* pl) {
     default: p.NS = 16; p.NW = 16; break;
   }
   // Per-channel layout with up to 32 states: one wave per 8 channels, no barriers.
-  p.kernel = (d->layout == SSM_LAYOUT_BDL && p.Npad <= 32) ? 1 : 0;
+  // (Its lane offsets along time are 32-bit: sequences up to 2^26 steps.)
+  p.kernel = (d->layout == SSM_LAYOUT_BDL && p.Npad <= 32 && d->seqlen <= ((int64_t)1 << 26)) ? 1 : 0;
   int64_t units, target;
   if (p.kernel == 1) {
     p.NS = p.Npad / 8;
@@ -117,9 +118,17 @@ int make_plan(const ssm_dims_t* d, Plan* pl) {
   if ((int64_t)p.grid_rows > 0x7fffffff) return SSM_ERR_BAD_DIMS;
   p.nseg = choose_segments(d->seqlen, units, target, p.TB, &p.seg_len);
   p.vec_ok = (d->layout == SSM_LAYOUT_BDL) && (d->seqlen % 4 == 0);
-  p.ws_bytes = p.nseg > 1 ? (size_t)2 * (size_t)(p.nseg - 1) * (size_t)d->batch * (size_t)p.Npad *
-                                    (size_t)d->dim * sizeof(float)
-                          : 0;
+  p.seg_bytes = p.nseg > 1 ? (size_t)2 * (size_t)(p.nseg - 1) * (size_t)d->batch * (size_t)p.Npad *
+                                     (size_t)d->dim * sizeof(float)
+                           : 0;
+  if (p.kernel == 1) {
+    p.nblk = (d->seqlen + p.TB - 1) / p.TB;
+    if (p.nblk > 0x7fffffff) return SSM_ERR_BAD_DIMS;
+    p.bc_bytes = (size_t)d->batch * (size_t)d->ngroups * (size_t)p.nblk * (size_t)p.TB * 2 * (size_t)p.Npad *
+                 sizeof(float);
+    p.bc_bytes = (p.bc_bytes + 255) & ~(size_t)255;
+  }
+  p.ws_bytes = p.bc_bytes + p.seg_bytes;
   *pl = p;
   return SSM_OK;
 }
@@ -217,9 +226,11 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   ssm::KParams kp{};
   kp.u = u; kp.delta = delta; kp.A = A; kp.B = B; kp.C = C; kp.D = D; kp.z = z; kp.bias = delta_bias;
   kp.h0 = h0; kp.y = y; kp.h_last = h_last;
-  const size_t half = pl.ws_bytes / 2 / sizeof(float);
-  kp.wsP = pl.ws_bytes ? (float*)ws : nullptr;
-  kp.wsH = pl.ws_bytes ? (float*)ws + half : nullptr;
+  const size_t half = pl.seg_bytes / 2 / sizeof(float);
+  kp.bct = pl.bc_bytes ? (float*)ws : nullptr;
+  kp.nblk = pl.nblk;
+  kp.wsP = pl.seg_bytes ? (float*)((char*)ws + pl.bc_bytes) : nullptr;
+  kp.wsH = pl.seg_bytes ? kp.wsP + half : nullptr;
   kp.L = dims->seqlen; kp.seg_len = pl.seg_len; kp.nseg = pl.nseg;
   kp.batch = (int)dims->batch; kp.dim = (int)dims->dim; kp.N = (int)dims->dstate; kp.Npad = pl.Npad;
   kp.H = (int)Hn; kp.P = bdl ? 1 : (int)dims->headdim; kp.G = (int)dims->ngroups;

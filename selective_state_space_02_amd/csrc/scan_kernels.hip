@@ -39,6 +39,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- element I/O
 // Global loads are issued as raw bits one time block ahead (so their latency hides
@@ -542,16 +543,19 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
 // each other: there is no workgroup barrier.  A time block is 32 steps; lane k of a
 // row loads, prepares (step size, dt*u) and finishes (readout sum, D*u, gate, store)
 // steps 4k..4k+3 of its row, and shares the prepared values with the other lanes of
-// the row through a per-wave LDS tile.  B_t/C_t of the block are staged per wave in
-// LDS.  The readout partial sums of the 8 lanes of a row are combined through LDS.
-// Full blocks use vector loads issued one block ahead; the ragged last block of a
-// segment is loaded element by element after the main loop.
+// the row through a per-wave LDS tile.  B_t/C_t of the block come from a tile that
+// bc_tile_kernel has already converted to fp32 in the LDS order, so staging them is
+// a straight copy.  The readout partial sums of the 8 lanes of a row are combined
+// through LDS.  u/delta/z/y are addressed as a wave-uniform row base plus a 32-bit
+// lane offset.  Full blocks use vector loads issued one block ahead; the ragged last
+// block of a segment is loaded element by element after the main loop.
 namespace rg {
 constexpr int LPR = 8;          // lanes per row
 constexpr int RPW = 64 / LPR;   // rows per wave
 constexpr int TB = 4 * LPR;     // steps per block (4 per lane)
 constexpr int TP = TB + 4;      // padded LDS row stride
 constexpr int WPG = 4;          // waves per workgroup (independent; packing only)
+template <int NS> constexpr int bc_tile() { return TB * 2 * LPR * NS; }   // floats per B/C tile
 }  // namespace rg
 
 // order the wave's own LDS writes before its reads of other lanes' data
@@ -561,21 +565,46 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// B_t, C_t of one (batch item, group, time block) as the tile the row-group kernel
+// copies into LDS: [t (32)][k (8)][B of states k*NS..k*NS+NS-1, then C of them],
+// fp32, zero for states >= N and steps >= L.  Grid (time blocks, G, batch).
+template <typename IO, int NS>
+__global__ void __launch_bounds__(256) bc_tile_kernel(KParams p) {
+  using namespace rg;
+  constexpr int NPAD = LPR * NS;
+  constexpr int TILE = bc_tile<NS>();
+  const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int64_t t0 = (int64_t)blk * TB;
+  float* dst = p.bct + ((int64_t)(b * p.G + g) * p.nblk + blk) * TILE;
+  const int64_t src_row = ((int64_t)b * p.G + g) * p.N;
+  for (int i = threadIdx.x; i < NPAD * TB; i += 256) {
+    const int n = i / TB, t = i % TB;                 // consecutive threads walk time: coalesced reads
+    float bv = 0.0f, cv = 0.0f;
+    if (n < p.N && t0 + t < p.L) {
+      const int64_t s = (src_row + n) * p.L + t0 + t;
+      bv = IO::cvt(IO::ld_bits(p.B, s));
+      cv = IO::cvt(IO::ld_bits(p.C, s));
+    }
+    float* o = dst + t * 2 * NPAD + (n / NS) * 2 * NS + n % NS;
+    o[0] = bv;
+    o[NS] = cv;
+  }
+}
+
 template <typename IO, int NS, int MODE, bool VECOK>
 __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
   using namespace rg;
-  using S = typename IO::S;
+  constexpr int kB = IO::kBytes;
   constexpr int NPAD = LPR * NS;
-  constexpr int SV = NPAD * TB / 64;                         // B (and C) values staged per lane
-  constexpr int NQ = SV * IO::kBytes / 16;                   // 16-byte loads per lane per tensor
-  static_assert(NQ >= 1 && (SV * IO::kBytes) % 16 == 0, "staging width");
-  using Raw4 = typename RawT<4 * IO::kBytes>::T;             // 4 steps of one tensor
+  constexpr int TILE_BC = bc_tile<NS>();
+  constexpr int NQ = TILE_BC / (64 * 4);                     // float4 of the B/C tile per lane
+  using Raw4 = typename RawT<4 * kB>::T;                     // 4 steps of one tensor
   constexpr int TILE = (RPW * LPR * TP > 2 * RPW * TP) ? RPW * LPR * TP : 2 * RPW * TP;
 
   __shared__ __attribute__((aligned(16))) float s_tile[WPG][TILE];        // dt|du, later partial sums
-  __shared__ __attribute__((aligned(16))) float s_bc[WPG][TB * 2 * NPAD];  // [t][k][B(NS) C(NS)]
+  __shared__ __attribute__((aligned(16))) float s_bc[WPG][TILE_BC];       // [t][k][B(NS) C(NS)]
 
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int row = lane / LPR, k = lane % LPR;
   const int rb = blockIdx.x * WPG + wv;
@@ -594,18 +623,32 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
   const int r0 = (rb % p.blocks_per_group) * RPW;
   const int rows_in = min(RPW, p.rows_per_group - r0);
   const bool row_ok = row < rows_in;
-  const int d = g * p.rows_per_group + r0 + (row_ok ? row : 0);   // clamped to a valid channel
+  // Lanes of rows past the end of the group compute row 0 of the wave again (same
+  // inputs, same arithmetic, same order) and store the identical values to the
+  // same places, so the loop needs no store mask.
+  const int row_e = row_ok ? row : 0;
+  const int d0 = g * p.rows_per_group + r0;                  // first channel of the wave
+  const int d = d0 + row_e;
+
+  // wave-uniform row base (bytes, SGPRs) + 32-bit lane offset (row < 8, L < 2^26)
+  const int64_t base = ((int64_t)b * p.dim + d0) * L * kB;
+  const char* const pu = (const char*)p.u + base;
+  const char* const pdl = (const char*)p.delta + base;
+  const char* const pz = (const char*)p.zsrc + base;
+  char* const py = (char*)p.y + base;
+  const uint32_t loff = ((uint32_t)row_e * (uint32_t)L + 4u * (uint32_t)k) * kB;
+  const f32x4* const tiles = (const f32x4*)(p.bct + (int64_t)(b * p.G + g) * p.nblk * TILE_BC);
 
   // ---- states n = k*NS + j of channel d
   float h[NS], A2[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int n = k * NS + j;
-    const bool ok = row_ok && n < p.N;
+    const bool ok = n < p.N;
     h[j] = (MODE == 0 && ok && p.h0) ? p.h0[((int64_t)b * p.dim + d) * p.N + n] : 0.0f;
     A2[j] = ok ? p.A[(int64_t)d * p.N + n] * kLog2e : 0.0f;
   }
-  if (MODE == 0 && seg > 0 && row_ok) {
+  if (MODE == 0 && seg > 0) {
     for (int s2 = 0; s2 < seg; ++s2) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
@@ -614,20 +657,13 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
       }
     }
   }
-  const float bias = (p.bias && row_ok) ? p.bias[d] : 0.0f;
-  const float Dd = (p.D && row_ok) ? p.D[d] : 0.0f;
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const float Dd = p.D ? p.D[d] : 0.0f;
   float sum_dt = 0.0f;
 
-  const int64_t xrow = ((int64_t)b * p.dim + d) * L;          // start of this row in u/delta/z/y
-  const int n_s = lane / (TB / SV);                           // staging: state and first step
-  const int t_s = (lane % (TB / SV)) * SV;
-  const int n_sc = n_s < p.N ? n_s : 0;                       // clamped state for loads
-  const int64_t brow = (((int64_t)b * p.G + g) * p.N + n_sc) * L;   // B/C row of that state
-
   // --------------------------------------------------------- one time block
-  // xin: delta/u/z of steps 4k..4k+3 (fp32); bcin: staged B then C values; nvalid steps
-  auto run_block = [&](int64_t tb, int nvalid, const float* raw, const float* uu, const float* zz,
-                       const float* bv, const float* cv) {
+  // raw/uu/zz: delta/u/z of steps 4k..4k+3 (fp32); the block's B/C tile is already in LDS
+  auto run_block = [&](int64_t tb, int nvalid, const float (&raw)[4], const float (&uu)[4], const float (&zz)[4]) {
     // prologue: step sizes and dt*u of this lane's 4 steps
     float dtv[4], duv[4];
 #pragma unroll
@@ -640,14 +676,6 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
     }
     *(float4*)&s_dt[row * TP + 4 * k] = make_float4(dtv[0], dtv[1], dtv[2], dtv[3]);
     *(float4*)&s_du[row * TP + 4 * k] = make_float4(duv[0], duv[1], duv[2], duv[3]);
-    // staged B/C of state n_s, steps t_s .. t_s+SV-1 (zero beyond N or past the block)
-#pragma unroll
-    for (int i = 0; i < SV; ++i) {
-      const bool ok = n_s < p.N && t_s + i < nvalid;
-      float* dst = &s_b[(t_s + i) * 2 * NPAD + (n_s / NS) * 2 * NS + n_s % NS];
-      dst[0] = ok ? bv[i] : 0.0f;
-      if (MODE == 0) dst[NS] = ok ? cv[i] : 0.0f;
-    }
     wave_lds_sync();
 
     // The recurrence over the 32 steps for this lane's NS states.  Software
@@ -659,7 +687,7 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
     float part[MODE == 0 ? TB : 1];
     float4 cur_dt, cur_du, nxt_dt, nxt_du;
     float cur_bc[4][NBC], nxt_bc[4][NBC];
-    auto load_group = [&](int t4, float4& dt4, float4& du4, float (&bc)[4][NBC]) {
+    auto load_group = [&](int t4, float4& dt4, float4& du4, float (&bcv)[4][NBC]) {
       dt4 = *(const float4*)&s_dt[row * TP + t4];
       du4 = *(const float4*)&s_du[row * TP + t4];
 #pragma unroll
@@ -668,13 +696,13 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
 #pragma unroll
         for (int j = 0; j < NBC; j += 2) {
           const float2 v = *(const float2*)&src[j];
-          bc[q][j] = v.x; bc[q][j + 1] = v.y;
+          bcv[q][j] = v.x; bcv[q][j + 1] = v.y;
         }
       }
     };
     // decay factors and inputs of one group, formed one group ahead of their use
     float ca[4][NS], cbx[4][NS], cC[4][NS], csd[4];
-    auto prep_group = [&](const float4& dt4, const float4& du4, const float (&bc)[4][NBC]) {
+    auto prep_group = [&](const float4& dt4, const float4& du4, const float (&bcv)[4][NBC]) {
       const float dtq[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
       const float duq[4] = {du4.x, du4.y, du4.z, du4.w};
 #pragma unroll
@@ -683,8 +711,8 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           ca[q][j] = __builtin_amdgcn_exp2f(dtq[q] * A2[j]);
-          cbx[q][j] = duq[q] * bc[q][j];
-          if (MODE == 0) cC[q][j] = bc[q][NS + j];
+          cbx[q][j] = duq[q] * bcv[q][j];
+          if (MODE == 0) cC[q][j] = bcv[q][NS + j];
         }
       }
     };
@@ -742,14 +770,13 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
         if (p.has_z) yv *= silu_f(zz[q]);
         ys[q] = yv;
       }
-      if (row_ok) {
-        if (VECOK && nvalid == TB) {
-          IO::template stv<4>(p.y, xrow + tb + 4 * k, ys);
-        } else {
+      char* const yb = py + tb * kB;
+      if (VECOK && nvalid == TB) {
+        IO::template stv<4>(yb + loff, 0, ys);
+      } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (4 * k + q < nvalid) IO::st(p.y, xrow + tb + 4 * k + q, ys[q]);
-        }
+        for (int q = 0; q < 4; ++q)
+          if (4 * k + q < nvalid) IO::st(yb + loff, q, ys[q]);
       }
     }
     wave_lds_sync();     // the next block rewrites the tiles this one read
@@ -760,54 +787,46 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
   if (VECOK) {
     const int64_t n_full = (t_seg1 - t_seg0) / TB;
     Raw4 pf_dt, pf_u, pf_z;
-    uint4 pf_b[NQ], pf_c[NQ];
+    f32x4 pf_bc[NQ];
     auto issue = [&](int64_t tb) {
-      pf_dt = *(const Raw4*)((const S*)p.delta + xrow + tb + 4 * k);
-      pf_u = *(const Raw4*)((const S*)p.u + xrow + tb + 4 * k);
-      if (MODE == 0) pf_z = *(const Raw4*)((const S*)p.zsrc + xrow + tb + 4 * k);
+      const int64_t ob = tb * kB;
+      pf_dt = *(const Raw4*)(pdl + ob + loff);
+      pf_u = *(const Raw4*)(pu + ob + loff);
+      if (MODE == 0) pf_z = *(const Raw4*)(pz + ob + loff);
+      const f32x4* tl = tiles + (tb / TB) * (TILE_BC / 4);
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        pf_b[i] = *(const uint4*)((const S*)p.B + brow + tb + t_s + i * (16 / IO::kBytes));
-        if (MODE == 0) pf_c[i] = *(const uint4*)((const S*)p.C + brow + tb + t_s + i * (16 / IO::kBytes));
-      }
+      for (int i = 0; i < NQ; ++i) pf_bc[i] = tl[lane + 64 * i];
     };
     if (n_full > 0) issue(t_blk);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): only prefetches are in flight inside the loop
     for (int64_t it = 0; it < n_full; ++it, t_blk += TB) {
-      float raw[4], uu[4], zz[4], bv[SV], cv[SV];
+      // take the prefetched block out of the prefetch registers, then refill them
+      float raw[4], uu[4], zz[4];
       IO::template unpack<4>(pf_dt, raw);
       IO::template unpack<4>(pf_u, uu);
       IO::template unpack<4>(pf_z, zz);
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        constexpr int E = 16 / IO::kBytes;
-        IO::template unpack<E>(*(const typename RawT<16>::T*)&pf_b[i], &bv[i * E]);
-        if (MODE == 0) IO::template unpack<E>(*(const typename RawT<16>::T*)&pf_c[i], &cv[i * E]);
-      }
-      if (it + 1 < n_full) issue(t_blk + TB);
-      run_block(t_blk, TB, raw, uu, zz, bv, cv);
+      for (int i = 0; i < NQ; ++i) ((f32x4*)s_b)[lane + 64 * i] = pf_bc[i];
+      issue(it + 1 < n_full ? t_blk + TB : t_blk);   // the last one re-reads this block (unused)
+      run_block(t_blk, TB, raw, uu, zz);
     }
   }
   // ------------------------------------------ remaining steps, element loads
   for (; t_blk < t_seg1; t_blk += TB) {
     const int nvalid = (int)min((int64_t)TB, t_seg1 - t_blk);
-    float raw[4], uu[4], zz[4], bv[SV], cv[SV];
+    const int64_t ob = t_blk * kB;
+    float raw[4], uu[4], zz[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bool ok = 4 * k + q < nvalid;
-      const int64_t i = xrow + t_blk + (ok ? 4 * k + q : 0);
-      raw[q] = IO::cvt(IO::ld_bits(p.delta, i));
-      uu[q] = IO::cvt(IO::ld_bits(p.u, i));
-      zz[q] = (MODE == 0) ? IO::cvt(IO::ld_bits(p.zsrc, i)) : 0.0f;
+      const int64_t i = 4 * k + q < nvalid ? q : -4 * k;     // clamped to step t_blk of the row
+      raw[q] = IO::cvt(IO::ld_bits(pdl + ob + loff, i));
+      uu[q] = IO::cvt(IO::ld_bits(pu + ob + loff, i));
+      zz[q] = (MODE == 0) ? IO::cvt(IO::ld_bits(pz + ob + loff, i)) : 0.0f;
     }
+    const f32x4* tl = tiles + (t_blk / TB) * (TILE_BC / 4);
 #pragma unroll
-    for (int i = 0; i < SV; ++i) {
-      const bool ok = t_s + i < nvalid;
-      const int64_t bi = brow + t_blk + (ok ? t_s + i : 0);
-      bv[i] = IO::cvt(IO::ld_bits(p.B, bi));
-      cv[i] = (MODE == 0) ? IO::cvt(IO::ld_bits(p.C, bi)) : 0.0f;
-    }
-    run_block(t_blk, nvalid, raw, uu, zz, bv, cv);
+    for (int i = 0; i < NQ; ++i) ((f32x4*)s_b)[lane + 64 * i] = tl[lane + 64 * i];
+    run_block(t_blk, nvalid, raw, uu, zz);
   }
 
   // ---- outputs of the pass
@@ -856,6 +875,11 @@ int launch_rowgroup_modes(const Plan& pl, const KParams& kp, hipStream_t st) {
   const dim3 block(rg::WPG * 64);
   const int total = kp.blocks_per_group * kp.G;
   const int gx = (total + rg::WPG - 1) / rg::WPG;
+  hipLaunchKernelGGL((bc_tile_kernel<IO, NS>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
+  {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
   if (pl.nseg > 1) {
     hipLaunchKernelGGL((rowgroup_kernel<IO, NS, 1, VECOK>), dim3(gx, kp.batch, pl.nseg - 1), block, 0, st, kp);
     hipError_t e = hipGetLastError();
@@ -867,7 +891,7 @@ int launch_rowgroup_modes(const Plan& pl, const KParams& kp, hipStream_t st) {
 
 template <typename IO, int NS>
 int launch_rowgroup(const Plan& pl, const KParams& kp, hipStream_t st) {
-  if (kp.L % 8 == 0) return launch_rowgroup_modes<IO, NS, true>(pl, kp, st);
+  if (kp.L % 4 == 0) return launch_rowgroup_modes<IO, NS, true>(pl, kp, st);
   return launch_rowgroup_modes<IO, NS, false>(pl, kp, st);
 }
 

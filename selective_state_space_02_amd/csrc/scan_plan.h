@@ -24,7 +24,10 @@ struct Plan {
   int blocks_per_group = 0;  // row blocks per channel group (BDL) or per head (BLHP)
   int grid_rows = 0;         // workgroups per batch item and segment
   bool vec_ok = false;       // 4-step vector loads allowed along time (BDL)
-  size_t ws_bytes = 0;
+  int64_t nblk = 0;          // row-group kernel: 32-step time blocks per sequence
+  size_t bc_bytes = 0;       // row-group kernel: fp32 B/C tiles (start of the workspace)
+  size_t seg_bytes = 0;      // segment aggregates (after the tiles)
+  size_t ws_bytes = 0;       // total workspace
 };
 
 struct KParams {
@@ -42,6 +45,8 @@ struct KParams {
   float* h_last;
   float* wsP;   // [seg][b][n][d] decay product of each aggregated segment
   float* wsH;   // [seg][b][n][d] zero-start end state of each aggregated segment
+  float* bct;   // row-group kernel: [b][g][block] B/C tiles in LDS order (bc_tile_kernel)
+  int64_t nblk; // row-group kernel: time blocks per sequence
   int64_t L, seg_len;
   int batch, dim, N, Npad, H, P, G;
   int rows_per_group;    // BDL: dim / G;  BLHP: P

@@ -118,9 +118,16 @@ def test_workspace_too_small():
     assert call(d) == scan.SSM_ERR_WORKSPACE
 
 
+def bc_tile_bytes(batch, seqlen, npad, groups=1):
+    """fp32 B/C tiles of the row-group kernel: 32-step blocks x (B and C) x padded states."""
+    n = batch * groups * ((seqlen + 31) // 32) * 32 * 2 * npad * 4
+    return (n + 255) // 256 * 256
+
+
 def test_workspace_size_and_plan():
     d = dims(batch=4, seqlen=2048, dim=5120, dstate=16)               # 320 row blocks: no segments
-    assert scan.workspace_size(d) == 0
+    assert scan.workspace_size(d) == bc_tile_bytes(4, 2048, 16)
+    assert "seg_len=2048" in scan.describe(d)
     txt = scan.describe(d)
     assert "kernel=rowgroup" in txt and "layout=bdl" in txt and "NS=2" in txt
     d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # 40 row blocks: segmented
@@ -136,9 +143,11 @@ def test_workspace_size_and_plan():
 def test_segment_override_env(monkeypatch):
     d = dims(batch=4, seqlen=2048, dim=5120, dstate=16)
     monkeypatch.setenv("SSM_SCAN_SEGMENTS", "4")
-    assert scan.workspace_size(d) == 2 * 3 * 4 * 16 * 5120 * 4
+    assert scan.workspace_size(d) == bc_tile_bytes(4, 2048, 16) + 2 * 3 * 4 * 16 * 5120 * 4
     monkeypatch.setenv("SSM_SCAN_SEGMENTS", "1")
-    assert scan.workspace_size(d) == 0
+    assert scan.workspace_size(d) == bc_tile_bytes(4, 2048, 16)
+    d = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
+    assert scan.workspace_size(d) == 0                                 # workgroup kernel, one segment
 
 
 def test_binding_rejects_cpu_tensors():
