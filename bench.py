@@ -64,7 +64,7 @@ def algorithmic_bytes(case) -> int:
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in ("selective_state_space_02_amd/csrc/scan_kernels.hip", "selective_state_space_02_amd/csrc/scan_api.cpp",
-              "selective_state_space_02_amd/csrc/scan_plan.h"):
+              "selective_state_space_02_amd/csrc/scan_plan.h", "selective_state_space_02_amd/csrc/update_kernels.hip"):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -143,6 +143,115 @@ def cpu_baseline(case, budget_s: float = 12.0):
             "sample": f"{what}, all {case.seqlen} steps, {case.dstate} states: {el:.3e} elements in {dt:.2f} s"}
 
 
+def decode_bytes(case) -> int:
+    """State read and written once, every other input read once, y written once."""
+    T = case.tensors
+    total = 2 * case.batch * case.dim * case.dstate * 4
+    for k in ("u", "delta", "B", "C", "z", "A", "D", "delta_bias"):
+        if T[k] is not None:
+            total += T[k].numel() * T[k].element_size()
+    return total + T["u"].numel() * T["u"].element_size()
+
+
+def decode_step_tensors(case, dev):
+    """The workload's single time step in the state-update layouts."""
+    T = {k: (None if v is None else v.to(dev)) for k, v in case.tensors.items()}
+    if case.layout == "bdl":
+        pick = lambda x: None if x is None else x[:, :, 0].contiguous()
+        B, C = T["B"][..., 0].contiguous(), T["C"][..., 0].contiguous()
+    else:
+        pick = lambda x: None if x is None else x[:, 0].contiguous()
+        B, C = pick(T["B"]), pick(T["C"])
+    return dict(x=pick(T["u"]), delta=pick(T["delta"]), B=B, C=C, z=pick(T["z"]), A=T["A"], D=T["D"],
+                bias=T["delta_bias"], h=T["h0"])
+
+
+def cpu_baseline_decode(case, budget_s: float = 12.0):
+    """The fp64 oracle's one-step scan, repeated on the whole batch within the budget."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    T = case.tensors
+    io = case.io_dtype
+
+    def np_io(t):
+        if t is None:
+            return None
+        t = t.contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if io == "bf16" else t.numpy()
+
+    f = lambda t: None if t is None else t.contiguous().numpy()
+    args = (np_io(T["u"]), np_io(T["delta"]), f(T["A"]), np_io(T["B"]), np_io(T["C"]), f(T["D"]), np_io(T["z"]),
+            f(T["delta_bias"]), case.softplus, f(T["h0"]))
+    threads = oracle.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.scan_f64(*args, nthreads=threads, layout=case.layout, io_dtype=io, ngroups=case.ngroups)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt > budget_s or reps >= 200:
+            break
+    el = reps * case.elements
+    return {"value": el / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full one-step updates of the whole batch ({case.elements:.3e} elements each) "
+                      f"in {dt:.2f} s"}
+
+
+def bench_decode(args, case, dev):
+    """Single-token state update: one step = one ssm_state_update call over the whole batch."""
+    import torch
+
+    from selective_state_space_02_amd import scan
+
+    sets = []
+    for i in range(max(1, args.rotate) * 4):     # states of 4x the rotation count: > 256 MB in total
+        s = decode_step_tensors(case, dev)
+        s["h"] = s["h"].clone()
+        s["y"] = torch.empty_like(s["x"])
+        sets.append(s)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        scan.ssm_state_update(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["bias"], case.softplus,
+                              s["h"], layout=case.layout, inplace=True, y=s["y"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    abytes = decode_bytes(case)
+    achieved = abytes / (launch_ms * 1e-3) / 1e9
+    line = {
+        "metric": "selective state update (decode) elements/s (B·D·N) + achieved HBM GB/s vs MI355X peak",
+        "value": case.batch * case.dim * case.dstate / (ms_per_step * 1e-3),
+        "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "layout": case.layout, "io_dtype": case.io_dtype,
+                   "batch": case.batch, "dim": case.dim, "dstate": case.dstate, "nheads": case.nheads,
+                   "headdim": case.headdim, "ngroups": case.ngroups},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(args.workload),
+                     "kernel_ms": launch_ms, "algorithmic_bytes_per_launch": abytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(case, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,7 +273,7 @@ def main():
     import torch
 
     from selective_state_space_02_amd import scan
-    from selective_state_space_02_amd.inputs import make_config
+    from selective_state_space_02_amd.inputs import DECODE_CONFIGS, make_config
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -180,6 +289,8 @@ def main():
         return
 
     case = make_config(args.workload)
+    if args.workload in DECODE_CONFIGS:
+        return bench_decode(args, case, dev)
     sets = []
     for i in range(max(1, args.rotate)):
         T = {k: (None if v is None else v.to(dev)) for k, v in case.tensors.items()}

@@ -104,6 +104,26 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
                  const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream);
 
+/*
+ * Single-token state update (decode): one step of the same recurrence, the
+ * constant-time, constant-memory per-token update of generation
+ * («Mamba与SSM状态空间模型：一张摘要卡读完万页档案», section 线性扫描算法;
+ * «Mamba 选择性状态空间模型：亚二次复杂度大语言模型推理工程实践» §6.2).  It equals
+ * ssm_scan_fwd with seqlen = 1: dims->seqlen must be 1 (else SSM_ERR_BAD_DIMS),
+ * and the tensors have the scan layouts with the time axis of length 1:
+ *   SSM_LAYOUT_BDL : x, z, y, delta (batch, dim); B, C (batch, ngroups, dstate);
+ *                    A (dim, dstate); delta_bias, D (dim)
+ *   SSM_LAYOUT_BLHP: x, z, y (batch, nheads, headdim); delta (batch, nheads);
+ *                    B, C (batch, ngroups, dstate); A, delta_bias (nheads); D (dim)
+ *   h_in, h_out    : (batch, dim, dstate) float32.
+ * h_in NULL means a zero state; h_out NULL means the new state is not stored.
+ * h_out may be the same pointer as h_in (update in place) but must not overlap
+ * any other input or y.  Needs no workspace.  Errors as for ssm_scan_fwd.
+ */
+int ssm_state_update(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                     const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                     const float* h_in, float* h_out, void* y, const ssm_dims_t* dims, void* stream);
+
 /* Bytes of scratch ssm_scan_fwd needs for these dims (0 if none); 0 also for invalid dims. */
 size_t ssm_scan_workspace_size(const ssm_dims_t* dims);
 

@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssm_scan.so")
-SOURCES = [os.path.join(CSRC, "scan_api.cpp"), os.path.join(CSRC, "scan_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "scan_api.cpp"), os.path.join(CSRC, "scan_kernels.hip"),
+           os.path.join(CSRC, "update_kernels.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -46,12 +47,15 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     api_o = os.path.join(objdir, "scan_api.o")
-    ker_o = os.path.join(objdir, "scan_kernels.o")
     _run([HIPCC, *hipcc_flags(), "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c", "-o", api_o,
           SOURCES[0]], verbose)
-    _run([HIPCC, *hipcc_flags(), "-x", "hip", "-c", "-o", ker_o, SOURCES[1]], verbose)
+    objs = [api_o]
+    for src in SOURCES[1:]:
+        obj = os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + ".o")
+        _run([HIPCC, *hipcc_flags(), "-x", "hip", "-c", "-o", obj, src], verbose)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o], verbose)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -257,4 +257,51 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   return SSM_OK;
 }
 
+int ssm_state_update(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                     const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                     const float* h_in, float* h_out, void* y, const ssm_dims_t* dims, void* stream) {
+  ssm::g_hip_msg[0] = 0;
+  if (!x || !delta || !A || !B || !C || !y || !dims) return SSM_ERR_NULL_ARG;
+  ssm::Plan pl;
+  int rc = ssm::make_plan(dims, &pl);
+  if (rc != SSM_OK) return rc;
+  if (dims->seqlen != 1) return SSM_ERR_BAD_DIMS;
+  const void* ptrs[] = {x, delta, A, B, C, D, z, delta_bias, h_in, h_out, y};
+  for (const void* q : ptrs)
+    if (ssm::misaligned(q)) return SSM_ERR_ALIGN;
+
+  const size_t esz = dims->io_dtype == SSM_BF16 ? 2 : 4;
+  const size_t Bn = (size_t)dims->batch, Dm = (size_t)dims->dim, N = (size_t)dims->dstate;
+  const size_t G = (size_t)dims->ngroups;
+  const bool bdl = dims->layout == SSM_LAYOUT_BDL;
+  const size_t Hn = bdl ? Dm : (size_t)dims->nheads;
+  const size_t n_x = Bn * Dm * esz, n_dt = Bn * Hn * esz, n_bc = Bn * G * N * esz;
+  const size_t n_A = (bdl ? Dm * N : Hn) * 4, n_bias = Hn * 4, n_D = Dm * 4, n_state = Bn * Dm * N * 4;
+  struct Range { const void* p; size_t n; };
+  const Range inputs[] = {{x, n_x}, {delta, n_dt}, {A, n_A}, {B, n_bc}, {C, n_bc},
+                          {D, n_D}, {z, n_x}, {delta_bias, n_bias}, {h_in, n_state}};
+  for (const Range& r : inputs) {
+    if (ssm::overlaps(y, n_x, r.p, r.n)) return SSM_ERR_ALIAS;
+    // the state may be updated in place (h_out == h_in exactly), never partially overlapped
+    if (r.p == h_in && h_out == h_in) continue;
+    if (ssm::overlaps(h_out, n_state, r.p, r.n)) return SSM_ERR_ALIAS;
+  }
+  if (ssm::overlaps(y, n_x, h_out, n_state)) return SSM_ERR_ALIAS;
+
+  ssm::UParams up{};
+  up.x = x; up.delta = delta; up.A = A; up.B = B; up.C = C; up.D = D; up.z = z; up.bias = delta_bias;
+  up.h_in = h_in; up.h_out = h_out; up.y = y;
+  up.rows = (int64_t)Bn * (int64_t)Dm;
+  up.dim = (int)Dm; up.N = (int)N; up.H = (int)Hn; up.P = bdl ? 1 : (int)dims->headdim; up.G = (int)G;
+  up.rows_per_group = bdl ? (int)(Dm / G) : (int)dims->headdim;
+  up.heads_per_group = bdl ? 1 : (int)(Hn / G);
+  up.softplus = softplus_flag ? 1 : 0;
+  const int he = ssm::launch_update(up, dims->layout, dims->io_dtype, pl.Npad, stream);
+  if (he != 0) {
+    std::snprintf(ssm::g_hip_msg, sizeof ssm::g_hip_msg, "kernel launch: %s", hipGetErrorString((hipError_t)he));
+    return SSM_ERR_HIP;
+  }
+  return SSM_OK;
+}
+
 }  // extern "C"

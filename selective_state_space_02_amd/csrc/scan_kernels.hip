@@ -40,6 +40,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- element I/O
 // Global loads are issued as raw bits one time block ahead (so their latency hides
@@ -73,6 +74,11 @@ struct F32IO {
     if constexpr (V == 1) ((float*)p)[i] = v[0];
     if constexpr (V == 2) *(float2*)((float*)p + i) = make_float2(v[0], v[1]);
     if constexpr (V == 4) *(float4*)((float*)p + i) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  // 4 consecutive outputs with a streaming (nontemporal) store: written once, never re-read
+  __device__ static void stv4_stream(void* p, const float* v) {
+    const f32x4 w = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(w, (f32x4*)p);
   }
 };
 
@@ -118,6 +124,12 @@ struct BF16IO {
       *(uint2*)((uint16_t*)p + i) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c));
     }
   }
+  __device__ static void stv4_stream(void* p, const float* v) {
+    const bf16x2 a = {(__bf16)v[0], (__bf16)v[1]};
+    const bf16x2 c = {(__bf16)v[2], (__bf16)v[3]};
+    const u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
+    __builtin_nontemporal_store(w, (u32x2*)p);
+  }
 };
 
 // ------------------------------------------------------------ elementwise math
@@ -128,7 +140,7 @@ __device__ __forceinline__ float softplus_f(float r) {
   const float e = __builtin_amdgcn_exp2f(-fabsf(r) * kLog2e);
   const float w = 1.0f + e;
   const float err = e - (w - 1.0f);
-  return fmaxf(r, 0.0f) + fmaf(__builtin_amdgcn_logf(w), kLn2, err);
+  return (r > 0.0f ? r : 0.0f) + fmaf(__builtin_amdgcn_logf(w), kLn2, err);
 }
 
 // SiLU(z) = z / (1 + e^-z)
@@ -670,7 +682,8 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
     for (int q = 0; q < 4; ++q) {
       const bool ok = 4 * k + q < nvalid;
       const float rr = raw[q] + bias;
-      const float dt = ok ? (p.softplus ? softplus_f(rr) : rr) : 0.0f;
+      const float sp = softplus_f(rr);                        // branch-free: the 4 steps interleave
+      const float dt = ok ? (p.softplus ? sp : rr) : 0.0f;
       dtv[q] = dt;
       duv[q] = dt * uu[q];
     }
@@ -758,12 +771,18 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
         *(float4*)&s_part[(row * LPR + k) * TP + t4] =
             make_float4(part[t4], part[t4 + 1], part[t4 + 2], part[t4 + 3]);
       wave_lds_sync();
-      float ys[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      // sum of the 8 lanes' partials of this lane's 4 steps, as a pairwise tree
+      float4 pv[LPR];
 #pragma unroll
-      for (int kk = 0; kk < LPR; ++kk) {
-        const float4 v = *(const float4*)&s_part[(row * LPR + kk) * TP + 4 * k];
-        ys[0] += v.x; ys[1] += v.y; ys[2] += v.z; ys[3] += v.w;
-      }
+      for (int kk = 0; kk < LPR; ++kk) pv[kk] = *(const float4*)&s_part[(row * LPR + kk) * TP + 4 * k];
+#pragma unroll
+      for (int w = LPR / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int kk = 0; kk < w; ++kk) {
+          pv[kk].x += pv[kk + w].x; pv[kk].y += pv[kk + w].y;
+          pv[kk].z += pv[kk + w].z; pv[kk].w += pv[kk + w].w;
+        }
+      float ys[4] = {pv[0].x, pv[0].y, pv[0].z, pv[0].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float yv = fmaf(Dd, uu[q], ys[q]);
@@ -772,7 +791,7 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
       }
       char* const yb = py + tb * kB;
       if (VECOK && nvalid == TB) {
-        IO::template stv<4>(yb + loff, 0, ys);
+        IO::stv4_stream(yb + loff, ys);
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)

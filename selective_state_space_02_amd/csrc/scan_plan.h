@@ -58,10 +58,33 @@ struct KParams {
   int nseg;
 };
 
+// Arguments of the single-token state update (seqlen = 1).
+struct UParams {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  const float* h_in;
+  float* h_out;
+  void* y;
+  int64_t rows;          // batch * dim
+  int dim, N, H, P, G;
+  int rows_per_group;    // BDL: dim / G
+  int heads_per_group;   // BLHP: H / G
+  int softplus;
+};
+
 // Validates dims (no HIP call) and fills the plan; returns SSM_OK or an error code.
 int make_plan(const ssm_dims_t* d, Plan* plan);
 
 // Enqueue the kernels of a validated plan.  Returns a hipError_t value (0 = success).
 int launch_plan(const Plan& plan, const KParams& kp, void* stream);
+
+// Enqueue the state-update kernel.  Returns a hipError_t value (0 = success).
+int launch_update(const UParams& p, int layout, int io, int Npad, void* stream);
 
 }  // namespace ssm

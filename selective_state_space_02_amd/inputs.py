@@ -175,9 +175,27 @@ CONFIGS = {
 }
 CONFIG_IDS = {name: i + 1 for i, name in enumerate(CONFIGS)}
 
+# Single-token decode (state update) workloads: one step for a serving batch of
+# sequences, with the channel/state shapes of the Mamba-2.8B-shaped layer and of
+# the multi-head layer.  The state is read and written once per step.
+DECODE_CONFIGS = {
+    "mamba2p8b_decode": dict(layout="bdl", io_dtype="bf16", batch=64, seqlen=1, dim=5120, dstate=16,
+                             has_z=True, has_D=True, has_bias=True, has_h0=True, A_kind="lognormal",
+                             delta_kind="small"),
+    "mamba2_decode": dict(layout="blhp", io_dtype="bf16", batch=16, seqlen=1, dim=5120, dstate=128,
+                          nheads=80, headdim=64, ngroups=1, has_z=True, has_D=True, has_bias=True, has_h0=True,
+                          A_kind="head_uniform", delta_kind="small"),
+}
+DECODE_IDS = {name: 101 + i for i, name in enumerate(DECODE_CONFIGS)}
+
 
 def make_config(name: str, seed: Optional[int] = None) -> Case:
-    kw = dict(CONFIGS[name])
+    if name in DECODE_CONFIGS:
+        kw = dict(DECODE_CONFIGS[name])
+        base_id = DECODE_IDS[name]
+    else:
+        kw = dict(CONFIGS[name])
+        base_id = CONFIG_IDS[name]
     if seed is None:
-        seed = SEED_BASE + CONFIG_IDS[name]
+        seed = SEED_BASE + base_id
     return make_case(name, seed=seed, **kw)

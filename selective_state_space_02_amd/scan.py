@@ -30,7 +30,8 @@ SSM_ERR_ALIAS = -5
 SSM_ERR_WORKSPACE = -6
 SSM_ERR_HIP = -7
 
-EXPORTED = ("ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_strerror", "ssm_scan_describe", "ssm_scan_version")
+EXPORTED = ("ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_strerror", "ssm_scan_describe", "ssm_scan_version",
+            "ssm_state_update")
 
 
 class Dims(ctypes.Structure):
@@ -75,6 +76,9 @@ def load_library():
         lib.ssm_scan_describe.argtypes = [ctypes.POINTER(Dims), ctypes.c_char_p, ctypes.c_size_t]
         lib.ssm_scan_version.restype = ctypes.c_int
         lib.ssm_scan_version.argtypes = []
+        lib.ssm_state_update.restype = ctypes.c_int
+        lib.ssm_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                         ctypes.POINTER(Dims), vp]
         _lib = lib
     return _lib
 
@@ -188,3 +192,64 @@ def ssm_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
 def ssm_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None, **kw):
     """Convenience wrapper: returns (y, h_last)."""
     return ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, softplus, h0, **kw)
+
+
+def call_update_raw(x, delta, A, B, C, D, z, delta_bias, softplus, h_in, h_out, y, dims: Dims, stream=None) -> int:
+    """Direct ABI call of ssm_state_update with integer addresses (None = NULL).  Returns the status code."""
+    return int(load_library().ssm_state_update(x, delta, A, B, C, D, z, delta_bias, int(bool(softplus)), h_in, h_out,
+                                              y, ctypes.byref(dims), stream))
+
+
+def ssm_state_update(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                     D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                     delta_bias: Optional[torch.Tensor] = None, softplus: bool = True,
+                     h_in: Optional[torch.Tensor] = None, *, layout: str = "bdl",
+                     h_out: Optional[torch.Tensor] = None, inplace: bool = False, y: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One decode step on the GPU.  BDL: x, delta (B, D); BLHP: x (B, H, P), delta (B, H); B, C (B, G, N);
+    state (B, D, N) float32.  Returns (y, new state); with inplace=True the new state overwrites h_in."""
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssm_state_update runs on the GPU: tensors must be on a cuda device")
+    io = x.dtype
+    if io not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    if layout == "bdl":
+        Bsz, Dm = x.shape
+        H, P = 0, 0
+        shapes = dict(delta=(Bsz, Dm), A=(Dm, B.shape[2]), bias=(Dm,))
+    elif layout == "blhp":
+        Bsz, H, P = x.shape
+        Dm = H * P
+        shapes = dict(delta=(Bsz, H), A=(H,), bias=(H,))
+    else:
+        raise ValueError(layout)
+    G, N = B.shape[1], B.shape[2]
+    f32 = torch.float32
+    _check(delta, "delta", io, shapes["delta"], dev)
+    _check(A, "A", f32, shapes["A"], dev)
+    _check(B, "B", io, (Bsz, G, N), dev)
+    _check(C, "C", io, (Bsz, G, N), dev)
+    _check(D, "D", f32, (Dm,), dev)
+    _check(z, "z", io, tuple(x.shape), dev)
+    _check(delta_bias, "delta_bias", f32, shapes["bias"], dev)
+    _check(h_in, "h_in", f32, (Bsz, Dm, N), dev)
+    if inplace:
+        if h_in is None:
+            raise ValueError("inplace=True needs h_in")
+        h_out = h_in
+    elif h_out is None:
+        h_out = torch.empty((Bsz, Dm, N), dtype=f32, device=dev)
+    _check(h_out, "h_out", f32, (Bsz, Dm, N), dev)
+    if y is None:
+        y = torch.empty(tuple(x.shape), dtype=io, device=dev)
+    _check(y, "y", io, tuple(x.shape), dev)
+    dims = make_dims(layout, "bf16" if io == torch.bfloat16 else "f32", Bsz, 1, Dm, N, H, P, G)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.ssm_state_update(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                              int(bool(softplus)), _ptr(h_in), _ptr(h_out), _ptr(y), ctypes.byref(dims),
+                              ctypes.c_void_p(st.cuda_stream))
+    if rc != SSM_OK:
+        raise RuntimeError(f"ssm_state_update failed ({rc}): {strerror(rc)}")
+    return y, h_out

@@ -155,3 +155,24 @@ def test_binding_rejects_cpu_tensors():
     u = torch.zeros(1, 4, 8)
     with pytest.raises(ValueError):
         scan.ssm_scan_fwd(u, u, torch.zeros(4, 2), torch.zeros(1, 1, 2, 8), torch.zeros(1, 1, 2, 8))
+
+
+def call_update(dm, **over):
+    a = dict(P)
+    a.update(over)
+    return scan.call_update_raw(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], True,
+                                a["h0"], a["h_last"], a["y"], dm)
+
+
+def test_update_rejects_bad_arguments():
+    d1 = dims(seqlen=1)
+    for name in ["u", "delta", "A", "B", "C", "y"]:
+        assert call_update(d1, **{name: None}) == scan.SSM_ERR_NULL_ARG
+    assert call_update(dims(seqlen=2)) == scan.SSM_ERR_BAD_DIMS
+    assert call_update(dims(seqlen=1, dim=0)) == scan.SSM_ERR_BAD_DIMS
+    assert call_update(dims(seqlen=1, dstate=300)) == scan.SSM_ERR_UNSUPPORTED
+    assert call_update(d1, z=P["z"] + 4) == scan.SSM_ERR_ALIGN
+    assert call_update(d1, y=P["u"]) == scan.SSM_ERR_ALIAS
+    assert call_update(d1, h_last=P["h0"] + 16) == scan.SSM_ERR_ALIAS        # partial overlap of the state
+    assert call_update(d1, h_last=P["A"]) == scan.SSM_ERR_ALIAS
+    assert call_update(d1, y=P["h_last"]) == scan.SSM_ERR_ALIAS
