@@ -63,6 +63,8 @@ class _Dims(ctypes.Structure):
         ("ngroups", ctypes.c_int64),
         ("layout", ctypes.c_int32),
         ("io_dtype", ctypes.c_int32),
+        ("discretization", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -115,8 +117,11 @@ def _f32(a):
 
 def scan_f64(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None, *,
              layout="bdl", io_dtype="f32", ngroups=1, nheads=None, headdim=None,
-             t_out=None, nthreads=None, want_h_last=True):
-    """Run the C oracle.  Returns (y float64, h_last float64 or None)."""
+             t_out=None, nthreads=None, want_h_last=True, discretization="euler"):
+    """Run the C oracle.  Returns (y float64, h_last float64 or None).
+
+    discretization: "euler" (B̄ = Δ·B) or "zoh" (exact zero-order hold, B̄ = expm1(ΔA)/A·B).
+    """
     lay = LAYOUT_BDL if layout == "bdl" else LAYOUT_BLHP
     iod = 1 if io_dtype == "bf16" else 0
     u, delta, B, C, z = (_io(x, iod) for x in (u, delta, B, C, z))
@@ -129,7 +134,10 @@ def scan_f64(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, 
         Bsz, L, H, P = u.shape
         Dm = H * P
         N = B.shape[3]
-    dims = _Dims(Bsz, L, Dm, N, H if lay else 0, P if lay else 0, ngroups, lay, iod)
+    if discretization not in ("euler", "zoh"):
+        raise ValueError(discretization)
+    dims = _Dims(Bsz, L, Dm, N, H if lay else 0, P if lay else 0, ngroups, lay, iod,
+                 1 if discretization == "zoh" else 0, 0)
     if t_out is not None:
         t_out = np.ascontiguousarray(np.asarray(t_out, dtype=np.int64))
         T = len(t_out)
@@ -162,7 +170,7 @@ def _to_f64(a, io_dtype):
 
 
 def scan_numpy_f64(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None, *,
-                   layout="bdl", io_dtype="f32", ngroups=1):
+                   layout="bdl", io_dtype="f32", ngroups=1, discretization="euler"):
     """Same recurrence as scan_f64, written with numpy on (rows, N) arrays.
 
     Intended for small inputs (it loops over time in Python).
@@ -204,7 +212,12 @@ def scan_numpy_f64(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=
         r = r_t(t)
         dt = np.logaddexp(0.0, r) if softplus else r                  # log(1 + e^r)
         x = x_t(t)
-        h = np.exp(dt[..., None] * A_dn) * h + (dt * x)[..., None] * B_t(t)
+        if discretization == "zoh":                                   # expm1(ΔA)/A, Δ where A = 0
+            with np.errstate(divide="ignore", invalid="ignore"):
+                bbar = np.where(A_dn != 0.0, np.expm1(dt[..., None] * A_dn) / A_dn, dt[..., None])
+        else:
+            bbar = dt[..., None]
+        h = np.exp(dt[..., None] * A_dn) * h + (bbar * x[..., None]) * B_t(t)
         yt = np.einsum("bdn,bdn->bd", C_t(t), h) + Dv[None, :] * x
         if z_t is not None:
             zz = z_t(t)

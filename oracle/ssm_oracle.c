@@ -17,6 +17,9 @@
  *   Abar_t  = exp(Delta_t * A)                      «Mamba与SSM状态空间模型» section "离散化变换"
  *                                                    and "选择性机制" (e^{Δ_t A}); same page-1 §2.2
  *   Bbar_t x_t = Delta_t * B_t * x_t                «Mamba与SSM状态空间模型» "离散化变换" (B̄ = Δ B)
+ *     or, with discretization = 1, the exact zero-order hold of
+ *   Bbar_t = (Delta_t A)^-1 (exp(Delta_t A) - 1) Delta_t B_t   «Mamba 选择性状态空间模型» §2.2
+ *            = expm1(Delta_t A) / A * B_t  (Delta_t B_t when A = 0)
  *   h_t     = Abar_t * h_{t-1} + Bbar_t x_t         «Mamba 选择性状态空间模型» §2.2 and §4.1
  *   y_t     = C_t . h_t + D * x_t                   «Mamba 选择性状态空间模型» §2.2 (output eq.);
  *                                                    «Transformer架构遭遇颠覆性突破» §二.1
@@ -38,7 +41,10 @@
  *    which equals log(1+e^r) exactly in real arithmetic;
  *  - SiLU(z) = z / (1 + e^{-z});
  *  - the gate multiplies the whole S6 output including the D*x skip;
- *  - D, z, bias and h0 are optional (NULL means 0 / no gate / zero state).
+ *  - D, z, bias and h0 are optional (NULL means 0 / no gate / zero state);
+ *  - the zero-order-hold B̄ as printed on page 1 §2.2 lacks the factor Δ on B;
+ *    it is read as the exact hold of a constant input over one step, whose
+ *    first-order form is the Δ·B of the other pages.
  *
  * Parity pins for every function here live in tests/test_oracle_*.py.
  */
@@ -52,6 +58,8 @@ typedef struct {
   int64_t batch, seqlen, dim, dstate, nheads, headdim, ngroups;
   int32_t layout;   /* 0: (B,D,L) Mamba-1 layout; 1: (B,L,H,P) multi-head layout */
   int32_t io_dtype; /* 0: float32 storage; 1: bfloat16 storage (raw uint16 bits) */
+  int32_t discretization; /* 0: Bbar = Delta*B; 1: exact zero-order hold */
+  int32_t reserved;
 } oracle_dims;
 
 /* bfloat16 bits -> double: a bfloat16 is the upper half of a float32. */
@@ -122,7 +130,9 @@ static void scan_rows(const job_t* J) {
         const double Bn = load_io(J->B, i_bc + n * bc_stride, m->io_dtype);
         const double Cn = load_io(J->C, i_bc + n * bc_stride, m->io_dtype);
         const double abar = exp(dt * A);
-        h[n] = abar * h[n] + dt * Bn * x;
+        /* Bbar / B: Delta, or expm1(Delta A) / A for the exact hold (Delta when A = 0) */
+        const double bbar = (m->discretization == 1 && A != 0.0) ? expm1(dt * A) / A : dt;
+        h[n] = abar * h[n] + bbar * Bn * x;
         acc += Cn * h[n];
       }
       double yt = acc + (J->D ? (double)J->D[d] : 0.0) * x;
@@ -161,6 +171,7 @@ int oracle_scan_f64(const void* u, const void* delta, const float* A, const void
   if (!u || !delta || !A || !B || !C || !dims || !y) return -1;
   const oracle_dims m = *dims;
   if (m.batch <= 0 || m.seqlen <= 0 || m.dim <= 0 || m.dstate <= 0 || m.ngroups <= 0) return -1;
+  if (m.discretization != 0 && m.discretization != 1) return -1;
   if (m.layout == 1) {
     if (m.nheads <= 0 || m.headdim <= 0 || m.nheads * m.headdim != m.dim) return -1;
     if (m.nheads % m.ngroups) return -1;

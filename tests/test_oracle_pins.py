@@ -528,3 +528,88 @@ def test_input_generator_step_range():
     r = f64(c.tensors["delta"]) + f64(c.tensors["delta_bias"])[None, :, None]
     dt = np.logaddexp(0.0, r)
     assert dt.min() >= 0.999e-3 and dt.max() <= 0.1001
+
+
+# ---------------------------------------------------------------------------
+# Exact zero-order hold (discretization="zoh"): «Mamba 选择性状态空间模型» §2.2.
+# The hold is the exact solution of h' = A h + B x(t) when x is constant over
+# each step, so an ODE solver integrating the continuous system step by step
+# must reproduce it; its fixed point under a constant input is -B x / A for
+# any step size; it reduces to Δ·B when A = 0 and approaches Δ·B as Δ -> 0.
+# ---------------------------------------------------------------------------
+
+def _zoh_case(L, N, seed, step_lo=0.01, step_hi=0.8):
+    rng = np.random.default_rng(seed)
+    u = rng.normal(size=(1, 2, L)).astype(np.float32)
+    steps = rng.uniform(step_lo, step_hi, size=(1, 2, L)).astype(np.float32)
+    A = -rng.uniform(0.2, 3.0, size=(2, N)).astype(np.float32)
+    Bm = rng.normal(size=(1, 1, N, L)).astype(np.float32)
+    Cm = rng.normal(size=(1, 1, N, L)).astype(np.float32)
+    h0 = rng.normal(size=(1, 2, N)).astype(np.float32)
+    return u, steps, A, Bm, Cm, h0
+
+
+def test_zoh_matches_ode_integration():
+    import scipy.integrate
+    L, N = 12, 3
+    u, steps, A, Bm, Cm, h0 = _zoh_case(L, N, seed=5)
+    y, h = oracle.scan_f64(u, steps, A, Bm, Cm, None, None, None, False, h0, discretization="zoh")
+    for d in range(2):
+        hs = h0[0, d].astype(np.float64)
+        for t in range(L):
+            a = A[d].astype(np.float64)
+            drive = Bm[0, 0, :, t].astype(np.float64) * float(u[0, d, t])
+            sol = scipy.integrate.solve_ivp(lambda _s, x: a * x + drive, (0.0, float(steps[0, d, t])), hs,
+                                            method="DOP853", rtol=1e-13, atol=1e-15)
+            hs = sol.y[:, -1]
+            assert float(np.dot(Cm[0, 0, :, t].astype(np.float64), hs)) == pytest.approx(y[0, d, t], rel=1e-9,
+                                                                                       abs=1e-11)
+        np.testing.assert_allclose(h[0, d], hs, rtol=1e-9, atol=1e-11)
+
+
+def test_zoh_fixed_point_independent_of_step():
+    L, N = 4000, 4
+    u, steps, A, Bm, Cm, h0 = _zoh_case(L, N, seed=6, step_lo=0.05, step_hi=0.5)
+    u[:] = 0.625
+    Bm[:] = Bm[..., :1]                                               # constant B, input, varying steps
+    _, h = oracle.scan_f64(u, steps, A, Bm, Cm, None, None, None, False, h0, discretization="zoh")
+    want = -Bm[0, 0, :, 0].astype(np.float64)[None, :] * 0.625 / A.astype(np.float64)
+    np.testing.assert_allclose(h[0], want, rtol=1e-12, atol=1e-13)
+    _, h_euler = oracle.scan_f64(u, steps, A, Bm, Cm, None, None, None, False, h0)
+    assert np.abs(h_euler[0] - want).max() > 1e-3                     # the Δ·B form has another fixed point
+
+
+def test_zoh_limits():
+    L, N = 50, 5
+    u, steps, A, Bm, Cm, h0 = _zoh_case(L, N, seed=7)
+    A0 = A.copy()
+    A0[1, 2] = 0.0                                                    # one zero entry: exactly Δ·B there
+    ye, he = oracle.scan_f64(u, steps, A0 * 0, Bm, Cm, None, None, None, False, h0)
+    yz, hz = oracle.scan_f64(u, steps, A0 * 0, Bm, Cm, None, None, None, False, h0, discretization="zoh")
+    assert np.array_equal(ye, yz) and np.array_equal(he, hz)
+    tiny = np.full_like(steps, 1e-6)
+    ye, _ = oracle.scan_f64(u, tiny, A, Bm, Cm, None, None, None, False, h0)
+    yz, _ = oracle.scan_f64(u, tiny, A, Bm, Cm, None, None, None, False, h0, discretization="zoh")
+    rel = np.abs(yz - ye) / (np.abs(ye) + 1e-300)
+    assert 0 < np.median(rel) < 3e-6                                  # O(|ΔA|/2)
+
+
+@pytest.mark.parametrize("layout", ["bdl", "blhp"])
+def test_zoh_c_and_numpy_twins_agree(layout):
+    if layout == "bdl":
+        c = make_case(layout="bdl", io_dtype="bf16", batch=2, seqlen=40, dim=6, dstate=5, seed=21, has_h0=True,
+                      A_kind="lognormal", delta_kind="wide")
+    else:
+        c = make_case(layout="blhp", io_dtype="f32", batch=2, seqlen=40, dim=12, dstate=6, nheads=3, headdim=4,
+                      seed=22, has_h0=True, A_kind="head_uniform")
+    yc, hc = run_case(c, discretization="zoh")
+    T = c.tensors
+    yn, hn = oracle.scan_numpy_f64(np_io(T["u"], c.io_dtype), np_io(T["delta"], c.io_dtype), T["A"].numpy(),
+                                   np_io(T["B"], c.io_dtype), np_io(T["C"], c.io_dtype), T["D"].numpy(),
+                                   np_io(T["z"], c.io_dtype), T["delta_bias"].numpy(), c.softplus,
+                                   T["h0"].numpy(), layout=c.layout, io_dtype=c.io_dtype, ngroups=c.ngroups,
+                                   discretization="zoh")
+    np.testing.assert_allclose(yc, yn, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(hc, hn, rtol=1e-12, atol=1e-12)
+    ye, _ = run_case(c)
+    assert np.abs(ye - yc).max() > 1e-6                               # the flag changes the result
