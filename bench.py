@@ -36,15 +36,21 @@ TRANS_SLOTS = 4                                               # exp2/log2/rcp is
 #  per (b,d,t)  : softplus [bias add, 1+e add, exp, log], dt*u [mul], D*u [fma],
 #                 SiLU gate [exp, 1+e add, rcp, z*s mul, y*s mul]
 #  multi-head layout: exp(dt*A) is per (b,t,h), so per element only dt*u*B, h update, readout.
-def algorithmic_slots(case) -> float:
+#  exact zero-order hold (--discretization zoh): per (b,d,t,n) in the per-channel layout, x = dt*A [mul],
+#                 expm1 from the exp [add], divide by x [rcp + mul], scale B̄ [mul]; per (b,t,h) in the
+#                 multi-head layout (the factor is per head).
+ZOH_SLOTS = 4 + TRANS_SLOTS
+
+
+def algorithmic_slots(case, zoh=False) -> float:
     Bsz, L, Dm, N = case.batch, case.seqlen, case.dim, case.dstate
     has_z = case.tensors["z"] is not None
     per_row_step = (2 + 2 * TRANS_SLOTS) + 2 + ((3 + 2 * TRANS_SLOTS) if has_z else 0)
     if case.layout == "bdl":
-        per_elem = 4 + TRANS_SLOTS
+        per_elem = 4 + TRANS_SLOTS + (ZOH_SLOTS if zoh else 0)
         return Bsz * L * Dm * (N * per_elem + per_row_step)
     per_elem = 3
-    per_head_step = (2 + 2 * TRANS_SLOTS) + (1 + TRANS_SLOTS)  # softplus + exp(dt*A) per (b,t,h)
+    per_head_step = (2 + 2 * TRANS_SLOTS) + (1 + TRANS_SLOTS) + (ZOH_SLOTS if zoh else 0)
     per_chan_step = 2 + ((3 + 2 * TRANS_SLOTS) if has_z else 0)
     return Bsz * L * (Dm * (N * per_elem + per_chan_step) + case.nheads * per_head_step)
 
@@ -83,7 +89,7 @@ def load_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, budget_s: float = 12.0):
+def cpu_baseline(case, budget_s: float = 12.0, zoh: bool = False):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload: the first
     batch items (whole) or, if one item is already over budget, the first channels of
     item 0, always over the full sequence.  Returns the dict for the JSON line."""
@@ -122,7 +128,8 @@ def cpu_baseline(case, budget_s: float = 12.0):
             elems = nb * case.seqlen * nc * case.dstate
         threads = oracle.default_threads()
         t0 = time.perf_counter()
-        oracle.scan_f64(*args, nthreads=threads, layout=case.layout, io_dtype=io, ngroups=case.ngroups)
+        oracle.scan_f64(*args, nthreads=threads, layout=case.layout, io_dtype=io, ngroups=case.ngroups,
+                        discretization="zoh" if zoh else "euler")
         return time.perf_counter() - t0, elems, threads
 
     probe_ch = 64 if case.layout == "bdl" else case.headdim
@@ -259,6 +266,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--rotate", type=int, default=3, help="input sets rotated through (defeats the 256 MB MALL)")
+    ap.add_argument("--discretization", choices=("delta_b", "zoh"), default="delta_b",
+                    help="B̄ = Δ·B (the workloads' definition) or the exact zero-order hold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -298,7 +307,7 @@ def main():
         h = torch.empty((case.batch, case.dim, case.dstate), dtype=torch.float32, device=dev)
         sets.append((T, y, h))
     dims = scan.make_dims(case.layout, case.io_dtype, case.batch, case.seqlen, case.dim, case.dstate,
-                          case.nheads, case.headdim, case.ngroups)
+                          case.nheads, case.headdim, case.ngroups, args.discretization)
     ws_bytes = scan.workspace_size(dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     plan = scan.describe(dims)
@@ -307,7 +316,8 @@ def main():
     def step(i):
         T, y, h = sets[i % len(sets)]
         scan.ssm_scan_fwd(T["u"], T["delta"], T["A"], T["B"], T["C"], T["D"], T["z"], T["delta_bias"],
-                          case.softplus, T["h0"], layout=case.layout, y=y, h_last=h, workspace=ws, stream=stream)
+                          case.softplus, T["h0"], layout=case.layout, y=y, h_last=h, workspace=ws, stream=stream,
+                          discretization=args.discretization)
 
     for i in range(args.warmup):
         step(i)
@@ -330,7 +340,7 @@ def main():
     elements = case.elements
     value = elements / (ms_per_step * 1e-3)
 
-    slots = algorithmic_slots(case)
+    slots = algorithmic_slots(case, zoh=args.discretization == "zoh")
     achieved = slots / (launch_ms * 1e-3) / 1e12
     peak = VALU_SLOT_PEAK / 1e12
     abytes = algorithmic_bytes(case)
@@ -352,7 +362,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "layout": case.layout, "io_dtype": case.io_dtype, "batch": case.batch,
                    "seqlen": case.seqlen, "dim": case.dim, "dstate": case.dstate, "nheads": case.nheads,
-                   "headdim": case.headdim, "ngroups": case.ngroups, "plan": plan},
+                   "headdim": case.headdim, "ngroups": case.ngroups, "discretization": args.discretization,
+                   "plan": plan},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel_ms": launch_ms, "algorithmic_ops_per_launch": slots,
@@ -361,7 +372,7 @@ def main():
                 "frac": hbm_gbs / HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget, zoh=args.discretization == "zoh")
     print(json.dumps(line), flush=True)
 
 

@@ -9,6 +9,8 @@
  *   for every (batch b, channel d, state n), over t = 0 .. L-1:
  *     dt_t  = softplus(delta_t + delta_bias)      (or delta_t + delta_bias if softplus_flag == 0)
  *     h_t   = exp(dt_t * A) * h_{t-1} + dt_t * B_t * u_t          h_{-1} = h0 (or 0)
+ *             (with dims->discretization == SSM_DISC_ZOH the input term is the exact
+ *              zero-order hold expm1(dt_t * A) / A * B_t * u_t of «Mamba 选择性状态空间模型» §2.2)
  *     y_t   = (sum_n C_t[n] * h_t[n] + D * u_t) * SiLU(z_t)       (D, z optional)
  *   and h_last = h_{L-1}.
  *
@@ -71,10 +73,14 @@ extern "C" {
 #define SSM_F32 0
 #define SSM_BF16 1
 
+/* ssm_dims_t.discretization: how B̄ is formed from the step size */
+#define SSM_DISC_DELTA_B 0 /* B̄ = Δ·B (default; zero-initialised dims select it) */
+#define SSM_DISC_ZOH 1     /* exact zero-order hold: B̄ = (ΔA)^-1 (exp(ΔA) - 1) Δ·B = expm1(ΔA)/A · B */
+
 #define SSM_OK 0
 #define SSM_ERR_NULL_ARG -1    /* u, delta, A, B, C, y or dims is NULL */
 #define SSM_ERR_BAD_DIMS -2    /* a size <= 0, nheads*headdim != dim, groups do not divide, ... */
-#define SSM_ERR_UNSUPPORTED -3 /* unknown layout or io_dtype; dstate outside 1..256 */
+#define SSM_ERR_UNSUPPORTED -3 /* unknown layout, io_dtype or discretization; dstate outside 1..256 */
 #define SSM_ERR_ALIGN -4       /* a tensor pointer is not 16-byte aligned */
 #define SSM_ERR_ALIAS -5       /* y or h_last overlaps an input or each other */
 #define SSM_ERR_WORKSPACE -6   /* caller workspace smaller than ssm_scan_workspace_size */
@@ -92,6 +98,8 @@ typedef struct ssm_dims {
   int32_t io_dtype;  /* SSM_F32 or SSM_BF16 */
   void* workspace;          /* optional device scratch, see above */
   size_t workspace_bytes;   /* its size in bytes */
+  int32_t discretization;   /* SSM_DISC_DELTA_B (0) or SSM_DISC_ZOH (1); other values: SSM_ERR_UNSUPPORTED */
+  int32_t reserved;         /* must be 0 */
 } ssm_dims_t;
 
 /*

@@ -43,17 +43,27 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the host API (plain C++, -x c++) and the kernels (HIP), link one .so."""
+    """Compile the host API (plain C++, -x c++) and the kernels (HIP), link one .so.
+
+    scan_kernels.hip is compiled twice, once per discretization (-DSSM_ZOH=0/1); the
+    device compilations run in parallel.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     api_o = os.path.join(objdir, "scan_api.o")
-    _run([HIPCC, *hipcc_flags(), "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c", "-o", api_o,
-          SOURCES[0]], verbose)
-    objs = [api_o]
+    jobs = [([HIPCC, *hipcc_flags(), "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c", "-o",
+              api_o, SOURCES[0]], api_o)]
     for src in SOURCES[1:]:
-        obj = os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + ".o")
-        _run([HIPCC, *hipcc_flags(), "-x", "hip", "-c", "-o", obj, src], verbose)
-        objs.append(obj)
+        stem = os.path.splitext(os.path.basename(src))[0]
+        variants = [("_delta_b", ["-DSSM_ZOH=0"]), ("_zoh", ["-DSSM_ZOH=1"])] if stem == "scan_kernels" else [("", [])]
+        for suffix, defs in variants:
+            obj = os.path.join(objdir, stem + suffix + ".o")
+            jobs.append(([HIPCC, *hipcc_flags(), *defs, "-x", "hip", "-c", "-o", obj, src], obj))
+    with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    objs = [o for _, o in jobs]
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

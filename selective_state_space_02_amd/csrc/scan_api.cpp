@@ -67,6 +67,8 @@ int make_plan(const ssm_dims_t* d, Plan* pl) {
   if (!d || !pl) return SSM_ERR_NULL_ARG;
   if (d->layout != SSM_LAYOUT_BDL && d->layout != SSM_LAYOUT_BLHP) return SSM_ERR_UNSUPPORTED;
   if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (d->discretization != SSM_DISC_DELTA_B && d->discretization != SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
+  if (d->reserved != 0) return SSM_ERR_UNSUPPORTED;
   if (d->batch < 1 || d->seqlen < 1 || d->dim < 1 || d->dstate < 1 || d->ngroups < 1) return SSM_ERR_BAD_DIMS;
   if (d->dstate > 256) return SSM_ERR_UNSUPPORTED;
   if (d->batch > 65535 || d->dim > (int64_t)1 << 30 || d->seqlen > ((int64_t)1 << 40)) return SSM_ERR_BAD_DIMS;
@@ -82,6 +84,7 @@ int make_plan(const ssm_dims_t* d, Plan* pl) {
     groups_or_heads = d->nheads;
   }
   Plan p;
+  p.disc = d->discretization;
   p.layout = d->layout;
   p.io = d->io_dtype;
   const int64_t N = d->dstate;
@@ -133,6 +136,10 @@ int make_plan(const ssm_dims_t* d, Plan* pl) {
   return SSM_OK;
 }
 
+int launch_plan(const Plan& plan, const KParams& kp, void* stream) {
+  return plan.disc == SSM_DISC_ZOH ? launch_plan_zoh(plan, kp, stream) : launch_plan_delta_b(plan, kp, stream);
+}
+
 }  // namespace ssm
 
 extern "C" {
@@ -165,8 +172,10 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
   if (rc != SSM_OK) return rc;
   if (buf && buf_len) {
     std::snprintf(buf, buf_len,
-                  "kernel=%s layout=%s io=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d ws=%zu",
-                  p.kernel == 1 ? "rowgroup" : "workgroup", p.layout == SSM_LAYOUT_BDL ? "bdl" : "blhp", p.io == SSM_BF16 ? "bf16" : "f32", p.NS, p.NW, p.TB,
+                  "kernel=%s layout=%s io=%s disc=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d "
+                  "ws=%zu",
+                  p.kernel == 1 ? "rowgroup" : "workgroup", p.layout == SSM_LAYOUT_BDL ? "bdl" : "blhp",
+                  p.io == SSM_BF16 ? "bf16" : "f32", p.disc == SSM_DISC_ZOH ? "zoh" : "delta_b", p.NS, p.NW, p.TB,
                   p.Npad, p.grid_rows, (long long)dims->batch, p.nseg, (long long)p.seg_len, (int)p.vec_ok,
                   p.ws_bytes);
   }
@@ -296,6 +305,7 @@ int ssm_state_update(const void* x, const void* delta, const float* A, const voi
   up.rows_per_group = bdl ? (int)(Dm / G) : (int)dims->headdim;
   up.heads_per_group = bdl ? 1 : (int)(Hn / G);
   up.softplus = softplus_flag ? 1 : 0;
+  up.zoh = dims->discretization == SSM_DISC_ZOH ? 1 : 0;
   const int he = ssm::launch_update(up, dims->layout, dims->io_dtype, pl.Npad, stream);
   if (he != 0) {
     std::snprintf(ssm::g_hip_msg, sizeof ssm::g_hip_msg, "kernel launch: %s", hipGetErrorString((hipError_t)he));

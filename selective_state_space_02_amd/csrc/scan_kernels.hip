@@ -27,16 +27,37 @@
 // which is the chunk-carry form of the associative scan («Mamba 选择性状态空间模型»
 // §4.1 operator (a1,b1)(x)(a2,b2) = (a2 a1, a2 b1 + b2)).  Padded steps use
 // dt = 0 (a = 1, no input), padded states A = B = C = 0, so neither changes a state.
+//
+// This file is compiled twice: SSM_ZOH=0 gives the B̄ = Δ·B kernels
+// (launch_plan_delta_b), SSM_ZOH=1 the exact zero-order-hold ones (launch_plan_zoh,
+// «Mamba 选择性状态空间模型» §2.2), so neither build carries the other's arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "scan_plan.h"
+
+#ifndef SSM_ZOH
+#error "compile with -DSSM_ZOH=0 or -DSSM_ZOH=1"
+#endif
 
 namespace ssm {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr bool kZOH = SSM_ZOH != 0;
+
+// Exact zero-order hold: B̄ = expm1(x)/x * Δ·B with x = Δ·A.  y = x*log2(e) and
+// a = exp2(y) = e^x are already at hand.  For |x| >= 1/8, expm1 = a - 1 loses at
+// most one ulp of 1 against |a - 1| > 0.117 (< 6e-7 relative); below that the
+// degree-4 Taylor polynomial of expm1(x)/x is used (truncation < 5e-8 relative).
+// x = 0 (A = 0, or a padded state) gives exactly 1, i.e. B̄ = Δ·B.
+__device__ __forceinline__ float zoh_factor(float y, float a) {
+  const float x = y * kLn2;
+  const float poly = fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 120.0f, 1.0f / 24.0f), 1.0f / 6.0f), 0.5f), 1.0f);
+  const float big = (a - 1.0f) * __builtin_amdgcn_rcpf(x);
+  return fabsf(x) < 0.125f ? poly : big;
+}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -370,7 +391,9 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
           const float uu = IO::cvt(pm_u[k]);
           keep_u[k] = uu;
           keep_z[k] = IO::cvt(pm_z[k]);
-          s_du[t * 65 + lane] = dt * uu;
+          float du = dt * uu;
+          if (kZOH) du *= zoh_factor(dt * A2h, __builtin_amdgcn_exp2f(dt * A2h));   // per head: into du
+          s_du[t * 65 + lane] = du;
           if (lane == 0) {
             s_dt[t] = dt;
             s_a[t] = __builtin_amdgcn_exp2f(dt * A2h);
@@ -440,8 +463,15 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
           float acc = 0.0f;
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
-            const float a = (LAYOUT == 0) ? __builtin_amdgcn_exp2f(dtq[q] * A2[j]) : a_head;
-            h[j] = fmaf(a, h[j], duq[q] * bcv[qq][j]);
+            float a, bx = duq[q] * bcv[qq][j];
+            if (LAYOUT == 0) {
+              const float y = dtq[q] * A2[j];
+              a = __builtin_amdgcn_exp2f(y);
+              if (kZOH) bx *= zoh_factor(y, a);
+            } else {
+              a = a_head;                                   // the hold factor is already in du (per head)
+            }
+            h[j] = fmaf(a, h[j], bx);
             if (MODE == 0) acc = fmaf(bcv[qq][NS + j], h[j], acc);
           }
           yq[q] = acc;
@@ -723,8 +753,10 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
         csd[q] = dtq[q];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          ca[q][j] = __builtin_amdgcn_exp2f(dtq[q] * A2[j]);
+          const float y = dtq[q] * A2[j];
+          ca[q][j] = __builtin_amdgcn_exp2f(y);
           cbx[q][j] = duq[q] * bcv[q][j];
+          if (kZOH) cbx[q][j] *= zoh_factor(y, ca[q][j]);
           if (MODE == 0) cC[q][j] = bcv[q][NS + j];
         }
       }
@@ -934,7 +966,11 @@ int launch_io(const Plan& pl, const KParams& kp, hipStream_t st) {
 
 }  // namespace
 
-int launch_plan(const Plan& pl, const KParams& kp, void* stream) {
+#if SSM_ZOH
+int launch_plan_zoh(const Plan& pl, const KParams& kp, void* stream) {
+#else
+int launch_plan_delta_b(const Plan& pl, const KParams& kp, void* stream) {
+#endif
   hipStream_t st = (hipStream_t)stream;
   if (pl.layout == SSM_LAYOUT_BDL) {
     return pl.io == SSM_BF16 ? launch_io<0, BF16IO>(pl, kp, st) : launch_io<0, F32IO>(pl, kp, st);

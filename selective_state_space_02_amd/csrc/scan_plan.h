@@ -17,6 +17,7 @@ namespace ssm {
 
 struct Plan {
   int kernel = 0;            // 0: workgroup kernel (64 rows, states over waves); 1: row-group kernel
+  int disc = 0;              // SSM_DISC_DELTA_B or SSM_DISC_ZOH
   int layout = 0, io = 0;
   int NS = 0, NW = 0, TB = 0, Npad = 0;
   int nseg = 1;
@@ -76,13 +77,17 @@ struct UParams {
   int rows_per_group;    // BDL: dim / G
   int heads_per_group;   // BLHP: H / G
   int softplus;
+  int zoh;               // exact zero-order hold for B̄
 };
 
 // Validates dims (no HIP call) and fills the plan; returns SSM_OK or an error code.
 int make_plan(const ssm_dims_t* d, Plan* plan);
 
 // Enqueue the kernels of a validated plan.  Returns a hipError_t value (0 = success).
+// scan_kernels.hip is compiled once per discretization; launch_plan picks the build.
 int launch_plan(const Plan& plan, const KParams& kp, void* stream);
+int launch_plan_delta_b(const Plan& plan, const KParams& kp, void* stream);
+int launch_plan_zoh(const Plan& plan, const KParams& kp, void* stream);
 
 // Enqueue the state-update kernel.  Returns a hipError_t value (0 = success).
 int launch_update(const UParams& p, int layout, int io, int Npad, void* stream);

@@ -109,7 +109,14 @@ __global__ void __launch_bounds__(256) state_update_kernel(UParams p) {
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      hv[i][j] = fmaf(__builtin_amdgcn_exp2f(dt * Av[i][j] * kLog2e), hv[i][j], dtx * Bv[i][j]);
+      const float x = dt * Av[i][j];
+      const float a = __builtin_amdgcn_exp2f(x * kLog2e);
+      float bx = dtx * Bv[i][j];
+      if (p.zoh) {   // exact zero-order hold: times expm1(x)/x (Taylor below |x| = 1/8)
+        const float poly = fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 120.0f, 1.0f / 24.0f), 1.0f / 6.0f), 0.5f), 1.0f);
+        bx *= fabsf(x) < 0.125f ? poly : (a - 1.0f) * __builtin_amdgcn_rcpf(x);
+      }
+      hv[i][j] = fmaf(a, hv[i][j], bx);
       acc = fmaf(Cv[i][j], hv[i][j], acc);
     }
 #pragma unroll

@@ -20,6 +20,9 @@ SSM_LAYOUT_BDL = 0
 SSM_LAYOUT_BLHP = 1
 SSM_F32 = 0
 SSM_BF16 = 1
+SSM_DISC_DELTA_B = 0
+SSM_DISC_ZOH = 1
+DISCRETIZATIONS = {"delta_b": SSM_DISC_DELTA_B, "zoh": SSM_DISC_ZOH}
 
 SSM_OK = 0
 SSM_ERR_NULL_ARG = -1
@@ -47,6 +50,8 @@ class Dims(ctypes.Structure):
         ("io_dtype", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("discretization", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -88,10 +93,10 @@ def strerror(code: int) -> str:
 
 
 def make_dims(layout: str, io_dtype: str, batch: int, seqlen: int, dim: int, dstate: int,
-              nheads: int = 0, headdim: int = 0, ngroups: int = 1) -> Dims:
+              nheads: int = 0, headdim: int = 0, ngroups: int = 1, discretization: str = "delta_b") -> Dims:
     return Dims(batch, seqlen, dim, dstate, nheads, headdim, ngroups,
                 SSM_LAYOUT_BDL if layout == "bdl" else SSM_LAYOUT_BLHP,
-                SSM_BF16 if io_dtype == "bf16" else SSM_F32, None, 0)
+                SSM_BF16 if io_dtype == "bf16" else SSM_F32, None, 0, DISCRETIZATIONS[discretization], 0)
 
 
 def workspace_size(dims: Dims) -> int:
@@ -135,8 +140,10 @@ def ssm_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
                  h0: Optional[torch.Tensor] = None, *, layout: str = "bdl", ngroups: int = 1,
                  y: Optional[torch.Tensor] = None, h_last: Optional[torch.Tensor] = None,
                  want_h_last: bool = True, workspace: Optional[torch.Tensor] = None,
-                 stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Selective scan on the GPU.  Shapes as in include/ssm_scan.h; returns (y, h_last)."""
+                 stream: Optional[torch.cuda.Stream] = None,
+                 discretization: str = "delta_b") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Selective scan on the GPU.  Shapes as in include/ssm_scan.h; returns (y, h_last).
+    discretization: "delta_b" (B̄ = Δ·B) or "zoh" (exact zero-order hold)."""
     lib = load_library()
     dev = u.device
     if dev.type != "cuda":
@@ -173,7 +180,7 @@ def ssm_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
     if h_last is None and want_h_last:
         h_last = torch.empty((Bsz, Dm, N), dtype=f32, device=dev)
     _check(h_last, "h_last", f32, (Bsz, Dm, N), dev)
-    dims = make_dims(layout, "bf16" if io == torch.bfloat16 else "f32", Bsz, L, Dm, N, H, P, ngroups)
+    dims = make_dims(layout, "bf16" if io == torch.bfloat16 else "f32", Bsz, L, Dm, N, H, P, ngroups, discretization)
     need = int(lib.ssm_scan_workspace_size(ctypes.byref(dims)))
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -205,7 +212,8 @@ def ssm_state_update(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: t
                      delta_bias: Optional[torch.Tensor] = None, softplus: bool = True,
                      h_in: Optional[torch.Tensor] = None, *, layout: str = "bdl",
                      h_out: Optional[torch.Tensor] = None, inplace: bool = False, y: Optional[torch.Tensor] = None,
-                     stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                     stream: Optional[torch.cuda.Stream] = None,
+                     discretization: str = "delta_b") -> Tuple[torch.Tensor, torch.Tensor]:
     """One decode step on the GPU.  BDL: x, delta (B, D); BLHP: x (B, H, P), delta (B, H); B, C (B, G, N);
     state (B, D, N) float32.  Returns (y, new state); with inplace=True the new state overwrites h_in."""
     lib = load_library()
@@ -245,7 +253,7 @@ def ssm_state_update(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: t
     if y is None:
         y = torch.empty(tuple(x.shape), dtype=io, device=dev)
     _check(y, "y", io, tuple(x.shape), dev)
-    dims = make_dims(layout, "bf16" if io == torch.bfloat16 else "f32", Bsz, 1, Dm, N, H, P, G)
+    dims = make_dims(layout, "bf16" if io == torch.bfloat16 else "f32", Bsz, 1, Dm, N, H, P, G, discretization)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
     rc = lib.ssm_state_update(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                               int(bool(softplus)), _ptr(h_in), _ptr(h_out), _ptr(y), ctypes.byref(dims),

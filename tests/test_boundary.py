@@ -176,3 +176,18 @@ def test_update_rejects_bad_arguments():
     assert call_update(d1, h_last=P["h0"] + 16) == scan.SSM_ERR_ALIAS        # partial overlap of the state
     assert call_update(d1, h_last=P["A"]) == scan.SSM_ERR_ALIAS
     assert call_update(d1, y=P["h_last"]) == scan.SSM_ERR_ALIAS
+
+
+def test_discretization_field():
+    d = dims()
+    assert "disc=delta_b" in scan.describe(d)
+    dz = dims()
+    dz.discretization = scan.SSM_DISC_ZOH
+    assert "disc=zoh" in scan.describe(dz)
+    assert scan.workspace_size(dz) == scan.workspace_size(d)
+    bad = dims()
+    bad.discretization = 2
+    assert call(bad) == scan.SSM_ERR_UNSUPPORTED
+    bad = dims(seqlen=1)
+    bad.reserved = 1
+    assert call_update(bad) == scan.SSM_ERR_UNSUPPORTED
