@@ -81,6 +81,10 @@ def _load():
         lib.oracle_scan_f64.restype = ctypes.c_int
         lib.oracle_scan_f64.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
                                         ctypes.POINTER(_Dims), vp, ctypes.c_int64, vp, vp, ctypes.c_int]
+        lib.oracle_conv_scan_f64.restype = ctypes.c_int
+        lib.oracle_conv_scan_f64.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             ctypes.c_int, vp, ctypes.POINTER(_Dims), vp, ctypes.c_int64, vp, vp,
+                                             ctypes.c_int]
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
@@ -117,10 +121,14 @@ def _f32(a):
 
 def scan_f64(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None, *,
              layout="bdl", io_dtype="f32", ngroups=1, nheads=None, headdim=None,
-             t_out=None, nthreads=None, want_h_last=True, discretization="euler"):
-    """Run the C oracle.  Returns (y float64, h_last float64 or None).
+             t_out=None, nthreads=None, want_h_last=True, discretization="euler",
+             conv_w=None, conv_b=None, conv_state_in=None, want_conv_state=False):
+    """Run the C oracle.  Returns (y float64, h_last float64 or None), plus the final
+    convolution state when want_conv_state.
 
     discretization: "euler" (B̄ = Δ·B) or "zoh" (exact zero-order hold, B̄ = expm1(ΔA)/A·B).
+    conv_w (D, K) [, conv_b (D,), conv_state_in (B, D, K-1)]: u is the raw input of a causal
+    depthwise convolution followed by SiLU ((B,D,L) layout only).
     """
     lay = LAYOUT_BDL if layout == "bdl" else LAYOUT_BLHP
     iod = 1 if io_dtype == "bf16" else 0
@@ -147,12 +155,22 @@ def scan_f64(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, 
     h_last = np.empty((Bsz, Dm, N), dtype=np.float64) if want_h_last else None
     if nthreads is None:
         nthreads = default_threads()
-    rc = _load().oracle_scan_f64(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                 _ptr(delta_bias), int(bool(softplus)), _ptr(h0), ctypes.byref(dims),
-                                 _ptr(t_out), ctypes.c_int64(0 if t_out is None else T), _ptr(y),
-                                 _ptr(h_last), int(nthreads))
+    K = 0
+    conv_out = None
+    if conv_w is not None:
+        conv_w = _f32(conv_w)
+        K = conv_w.shape[1]
+        conv_b, conv_state_in = _f32(conv_b), _f32(conv_state_in)
+        conv_out = np.zeros((Bsz, Dm, max(K - 1, 0)), dtype=np.float64)
+    rc = _load().oracle_conv_scan_f64(_ptr(u), _ptr(conv_w), _ptr(conv_b), int(K), _ptr(conv_state_in),
+                                      _ptr(conv_out), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(delta_bias), int(bool(softplus)), _ptr(h0), ctypes.byref(dims),
+                                      _ptr(t_out), ctypes.c_int64(0 if t_out is None else T), _ptr(y),
+                                      _ptr(h_last), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_scan_f64 rejected its arguments")
+    if want_conv_state:
+        return y, h_last, conv_out
     return y, h_last
 
 
@@ -170,12 +188,23 @@ def _to_f64(a, io_dtype):
 
 
 def scan_numpy_f64(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None, *,
-                   layout="bdl", io_dtype="f32", ngroups=1, discretization="euler"):
+                   layout="bdl", io_dtype="f32", ngroups=1, discretization="euler", conv_w=None, conv_b=None,
+                   conv_state_in=None):
     """Same recurrence as scan_f64, written with numpy on (rows, N) arrays.
 
     Intended for small inputs (it loops over time in Python).
     """
     u, delta, B, C, z = (_to_f64(x, io_dtype) for x in (u, delta, B, C, z))
+    if conv_w is not None:                                            # causal depthwise conv + SiLU on u
+        w = np.asarray(conv_w, np.float64)                            # (D, K)
+        K = w.shape[1]
+        Bsz_, Dm_, L_ = u.shape
+        left = np.zeros((Bsz_, Dm_, K - 1)) if conv_state_in is None else np.asarray(conv_state_in, np.float64)
+        xp = np.concatenate([left, u], axis=2)                        # (B, D, K-1+L)
+        c = np.zeros_like(u) + (0.0 if conv_b is None else np.asarray(conv_b, np.float64)[None, :, None])
+        for k in range(K):
+            c = c + w[None, :, k:k + 1] * xp[:, :, k:k + L_]
+        u = c / (1.0 + np.exp(-c))
     A = np.asarray(A, np.float64)
     if layout == "bdl":
         Bsz, Dm, L = u.shape

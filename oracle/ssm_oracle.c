@@ -42,6 +42,12 @@
  *  - SiLU(z) = z / (1 + e^{-z});
  *  - the gate multiplies the whole S6 output including the D*x skip;
  *  - D, z, bias and h0 are optional (NULL means 0 / no gate / zero state);
+ *  - the optional input stage (oracle_conv_scan_f64) is the Mamba block's 1-D
+ *    convolution then SiLU in front of the SSM («AI底层架构的一场革命», section
+ *    "Mamba Block：完整模块结构"; «Mamba与SSM状态空间模型», section "Mamba架构设计");
+ *    the pages give neither width nor padding: it is read as causal (step t sees
+ *    inputs t-K+1..t), depthwise (one filter of width K per channel, plus a bias),
+ *    with the K-1 inputs before t = 0 taken from a carried state (zeros if none);
  *  - the zero-order-hold B̄ as printed on page 1 §2.2 lacks the factor Δ on B;
  *    it is read as the exact hold of a constant input over one step, whose
  *    first-order form is the Δ·B of the other pages.
@@ -86,6 +92,9 @@ typedef struct {
   const void *u, *delta, *B, *C, *z;
   const float *A, *D, *bias, *h0;
   int softplus;
+  const float *conv_w, *conv_b, *conv_state_in; /* optional causal depthwise conv + SiLU stage */
+  int conv_k;
+  double* conv_state_out;
   oracle_dims dims;
   const int64_t* t_out; /* sorted list of time indices whose y is emitted; NULL: all */
   int64_t n_t_out;
@@ -101,12 +110,15 @@ static void scan_rows(const job_t* J) {
   const int64_t H = (m->layout == 1) ? m->nheads : Dm;
   const int64_t P = (m->layout == 1) ? m->headdim : 1;
   double* h = (double*)malloc(sizeof(double) * (size_t)N);
+  const int K = J->conv_k;                    /* 0: no input stage */
+  double win[16];                             /* the K-1 previous raw inputs, oldest first */
   (void)Bsz;
   for (int64_t row = J->row_begin; row < J->row_end; ++row) {
     const int64_t b = row / Dm, d = row % Dm;
     const int64_t hd = d / P, p = d % P;       /* head and position within head */
     const int64_t g = hd / (H / G);            /* group of this head / channel */
     for (int64_t n = 0; n < N; ++n) h[n] = J->h0 ? (double)J->h0[row * N + n] : 0.0;
+    for (int k = 0; k + 1 < K; ++k) win[k] = J->conv_state_in ? (double)J->conv_state_in[row * (K - 1) + k] : 0.0;
     int64_t k_out = 0;
     for (int64_t t = 0; t < L; ++t) {
       int64_t i_x, i_dt, i_bc;
@@ -123,7 +135,16 @@ static void scan_rows(const job_t* J) {
       const double bias = J->bias ? (double)J->bias[m->layout == 0 ? d : hd] : 0.0;
       const double r = load_io(J->delta, i_dt, m->io_dtype) + bias;
       const double dt = J->softplus ? oracle_softplus(r) : r;
-      const double x = load_io(J->u, i_x, m->io_dtype);
+      double x = load_io(J->u, i_x, m->io_dtype);
+      if (K > 0) {
+        /* causal depthwise convolution over the raw inputs t-K+1..t, then SiLU */
+        double c = J->conv_b ? (double)J->conv_b[d] : 0.0;
+        for (int k = 0; k + 1 < K; ++k) c += (double)J->conv_w[d * K + k] * win[k];
+        c += (double)J->conv_w[d * K + K - 1] * x;
+        for (int k = 0; k + 2 < K; ++k) win[k] = win[k + 1];
+        if (K > 1) win[K - 2] = x;
+        x = oracle_silu(c);
+      }
       double acc = 0.0;
       for (int64_t n = 0; n < N; ++n) {
         const double A = (m->layout == 0) ? (double)J->A[d * N + n] : (double)J->A[hd];
@@ -150,6 +171,8 @@ static void scan_rows(const job_t* J) {
     }
     if (J->h_last)
       for (int64_t n = 0; n < N; ++n) J->h_last[row * N + n] = h[n];
+    if (J->conv_state_out)
+      for (int k = 0; k + 1 < K; ++k) J->conv_state_out[row * (K - 1) + k] = win[k];
   }
   free(h);
 }
@@ -164,11 +187,34 @@ static void* scan_thread(void* arg) {
  * y has the layout of u with the time axis restricted to t_out (if given;
  * t_out must be strictly increasing).  h_last is (B, D, N) in float64.
  */
+int oracle_conv_scan_f64(const void* u, const float* conv_w, const float* conv_b, int conv_k,
+                         const float* conv_state_in, double* conv_state_out, const void* delta, const float* A,
+                         const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
+                         int softplus, const float* h0, const oracle_dims* dims, const int64_t* t_out,
+                         int64_t n_t_out, double* y, double* h_last, int nthreads);
+
 int oracle_scan_f64(const void* u, const void* delta, const float* A, const void* B, const void* C,
                     const float* D, const void* z, const float* delta_bias, int softplus,
                     const float* h0, const oracle_dims* dims, const int64_t* t_out, int64_t n_t_out,
                     double* y, double* h_last, int nthreads) {
+  return oracle_conv_scan_f64(u, NULL, NULL, 0, NULL, NULL, delta, A, B, C, D, z, delta_bias, softplus, h0, dims,
+                              t_out, n_t_out, y, h_last, nthreads);
+}
+
+/*
+ * Same scan with the raw input u first passed through the causal depthwise
+ * convolution (weights (D, conv_k) float32, bias (D) or NULL) and SiLU; the
+ * conv_k - 1 inputs before t = 0 come from conv_state_in (B, D, conv_k-1) or
+ * are 0, and conv_state_out (B, D, conv_k-1) receives the last conv_k - 1 raw
+ * inputs.  Only the (B,D,L) layout; conv_k in 1..16.
+ */
+int oracle_conv_scan_f64(const void* u, const float* conv_w, const float* conv_b, int conv_k,
+                         const float* conv_state_in, double* conv_state_out, const void* delta, const float* A,
+                         const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
+                         int softplus, const float* h0, const oracle_dims* dims, const int64_t* t_out,
+                         int64_t n_t_out, double* y, double* h_last, int nthreads) {
   if (!u || !delta || !A || !B || !C || !dims || !y) return -1;
+  if (conv_k < 0 || conv_k > 16 || (conv_k > 0 && (!conv_w || dims->layout != 0))) return -1;
   const oracle_dims m = *dims;
   if (m.batch <= 0 || m.seqlen <= 0 || m.dim <= 0 || m.dstate <= 0 || m.ngroups <= 0) return -1;
   if (m.discretization != 0 && m.discretization != 1) return -1;
@@ -195,6 +241,8 @@ int oracle_scan_f64(const void* u, const void* delta, const float* A, const void
     job_t* J = &jobs[i];
     J->u = u; J->delta = delta; J->B = B; J->C = C; J->z = z;
     J->A = A; J->D = D; J->bias = delta_bias; J->h0 = h0; J->softplus = softplus;
+    J->conv_w = conv_w; J->conv_b = conv_b; J->conv_k = conv_k;
+    J->conv_state_in = conv_state_in; J->conv_state_out = conv_state_out;
     J->dims = m; J->t_out = t_out; J->n_t_out = n_t_out; J->y = y; J->h_last = h_last;
     J->row_begin = rows * i / nthreads;
     J->row_end = rows * (i + 1) / nthreads;

@@ -613,3 +613,67 @@ def test_zoh_c_and_numpy_twins_agree(layout):
     np.testing.assert_allclose(hc, hn, rtol=1e-12, atol=1e-12)
     ye, _ = run_case(c)
     assert np.abs(ye - yc).max() > 1e-6                               # the flag changes the result
+
+
+# ---------------------------------------------------------------------------
+# Input stage: causal depthwise 1-D convolution + SiLU before the SSM
+# («AI底层架构的一场革命», section "Mamba Block：完整模块结构").
+# ---------------------------------------------------------------------------
+
+def _conv_case(L=37, Dm=3, K=4, seed=9):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(2, Dm, L)).astype(np.float32)
+    w = rng.normal(size=(Dm, K)).astype(np.float32)
+    b = rng.normal(size=(Dm,)).astype(np.float32)
+    steps = rng.uniform(0.01, 0.2, size=(2, Dm, L)).astype(np.float32)
+    A = -rng.uniform(0.5, 2.0, size=(Dm, 5)).astype(np.float32)
+    Bm = rng.normal(size=(2, 1, 5, L)).astype(np.float32)
+    Cm = rng.normal(size=(2, 1, 5, L)).astype(np.float32)
+    return x, w, b, steps, A, Bm, Cm
+
+
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_conv_stage_matches_numpy_convolve(K):
+    """With C = 0 and D = 1 the output is the stage itself: SiLU(conv(x) + bias)."""
+    x, w, b, steps, A, Bm, Cm = _conv_case(K=K)
+    Dv = np.ones(x.shape[1], np.float32)
+    y, _ = oracle.scan_f64(x, steps, A, Bm, np.zeros_like(Cm), Dv, None, None, False, None, conv_w=w, conv_b=b)
+    for bb in range(2):
+        for d in range(x.shape[1]):
+            c = np.convolve(x[bb, d].astype(np.float64), w[d, ::-1].astype(np.float64))[: x.shape[2]] + b[d]
+            np.testing.assert_allclose(y[bb, d], c / (1.0 + np.exp(-c)), rtol=1e-13, atol=1e-14)
+
+
+def test_conv_continuation_bitwise():
+    """scan(0..L) == scan(0..k) then scan(k..L) seeded with the final state and the conv state."""
+    x, w, b, steps, A, Bm, Cm = _conv_case(L=50)
+    h0 = np.random.default_rng(3).normal(size=(2, 3, 5)).astype(np.float32)
+    y, h = oracle.scan_f64(x, steps, A, Bm, Cm, None, None, None, True, h0, conv_w=w, conv_b=b)
+    k = 19
+    sl = lambda a, lo, hi: np.ascontiguousarray(a[..., lo:hi])
+    y1, h1, cs = oracle.scan_f64(sl(x, 0, k), sl(steps, 0, k), A, sl(Bm, 0, k), sl(Cm, 0, k), None, None, None,
+                                 True, h0, conv_w=w, conv_b=b, want_conv_state=True)
+    np.testing.assert_array_equal(cs, x[:, :, k - 3:k].astype(np.float64))     # the last K-1 raw inputs
+    y2, h2 = oracle.scan_f64(sl(x, k, 50), sl(steps, k, 50), A, sl(Bm, k, 50), sl(Cm, k, 50), None, None, None,
+                             True, h1.astype(np.float32), conv_w=w, conv_b=b, conv_state_in=cs.astype(np.float32))
+    # h1 and cs pass through float32 (exact for cs: raw float32 inputs; h1 rounds once)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=2), y, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(h2, h, rtol=1e-6, atol=1e-7)
+
+
+def test_conv_c_and_numpy_twins_agree():
+    c = make_case(layout="bdl", io_dtype="bf16", batch=2, seqlen=45, dim=6, dstate=7, seed=23, has_h0=True,
+                  A_kind="lognormal")
+    rng = np.random.default_rng(4)
+    w = rng.normal(size=(6, 4)).astype(np.float32)
+    b = rng.normal(size=(6,)).astype(np.float32)
+    st = rng.normal(size=(2, 6, 3)).astype(np.float32)
+    yc, hc = run_case(c, conv_w=w, conv_b=b, conv_state_in=st)
+    T = c.tensors
+    yn, hn = oracle.scan_numpy_f64(np_io(T["u"], c.io_dtype), np_io(T["delta"], c.io_dtype), T["A"].numpy(),
+                                   np_io(T["B"], c.io_dtype), np_io(T["C"], c.io_dtype), T["D"].numpy(),
+                                   np_io(T["z"], c.io_dtype), T["delta_bias"].numpy(), c.softplus,
+                                   T["h0"].numpy(), layout=c.layout, io_dtype=c.io_dtype, conv_w=w, conv_b=b,
+                                   conv_state_in=st)
+    np.testing.assert_allclose(yc, yn, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(hc, hn, rtol=1e-11, atol=1e-12)
