@@ -40,12 +40,15 @@ TRANS_SLOTS = 4                                               # exp2/log2/rcp is
 #                 expm1 from the exp [add], divide by x [rcp + mul], scale B̄ [mul]; per (b,t,h) in the
 #                 multi-head layout (the factor is per head).
 ZOH_SLOTS = 4 + TRANS_SLOTS
+#  fused input stage (--conv K): per (b,d,t) K fma for the causal conv, SiLU [exp, 1+e add, rcp, mul].
+def conv_slots(K):
+    return K + 2 + 2 * TRANS_SLOTS if K else 0
 
 
-def algorithmic_slots(case, zoh=False) -> float:
+def algorithmic_slots(case, zoh=False, conv_k=0) -> float:
     Bsz, L, Dm, N = case.batch, case.seqlen, case.dim, case.dstate
     has_z = case.tensors["z"] is not None
-    per_row_step = (2 + 2 * TRANS_SLOTS) + 2 + ((3 + 2 * TRANS_SLOTS) if has_z else 0)
+    per_row_step = (2 + 2 * TRANS_SLOTS) + 2 + ((3 + 2 * TRANS_SLOTS) if has_z else 0) + conv_slots(conv_k)
     if case.layout == "bdl":
         per_elem = 4 + TRANS_SLOTS + (ZOH_SLOTS if zoh else 0)
         return Bsz * L * Dm * (N * per_elem + per_row_step)
@@ -89,7 +92,7 @@ def load_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, budget_s: float = 12.0, zoh: bool = False):
+def cpu_baseline(case, budget_s: float = 12.0, zoh: bool = False, conv=None):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload: the first
     batch items (whole) or, if one item is already over budget, the first channels of
     item 0, always over the full sequence.  Returns the dict for the JSON line."""
@@ -128,8 +131,11 @@ def cpu_baseline(case, budget_s: float = 12.0, zoh: bool = False):
             elems = nb * case.seqlen * nc * case.dstate
         threads = oracle.default_threads()
         t0 = time.perf_counter()
+        extra = {}
+        if conv is not None:                              # the fused input stage, same channels
+            extra = dict(conv_w=conv[0][:nch], conv_b=conv[1][:nch])
         oracle.scan_f64(*args, nthreads=threads, layout=case.layout, io_dtype=io, ngroups=case.ngroups,
-                        discretization="zoh" if zoh else "euler")
+                        discretization="zoh" if zoh else "euler", **extra)
         return time.perf_counter() - t0, elems, threads
 
     probe_ch = 64 if case.layout == "bdl" else case.headdim
@@ -268,6 +274,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="input sets rotated through (defeats the 256 MB MALL)")
     ap.add_argument("--discretization", choices=("delta_b", "zoh"), default="delta_b",
                     help="B̄ = Δ·B (the workloads' definition) or the exact zero-order hold")
+    ap.add_argument("--conv", type=int, default=0, metavar="K",
+                    help="fuse a causal depthwise conv1d of width K (1..4) + SiLU in front of the scan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -313,8 +321,19 @@ def main():
     plan = scan.describe(dims)
     stream = torch.cuda.current_stream(dev)
 
+    conv = None
+    if args.conv:
+        gen = torch.Generator().manual_seed(20260999)
+        conv = ((torch.randn(case.dim, args.conv, generator=gen) * 0.5).to(dev),
+                (torch.randn(case.dim, generator=gen) * 0.2).to(dev))
+
     def step(i):
         T, y, h = sets[i % len(sets)]
+        if conv is not None:
+            scan.ssm_conv_scan_fwd(T["u"], conv[0], conv[1], T["delta"], T["A"], T["B"], T["C"], T["D"], T["z"],
+                                   T["delta_bias"], case.softplus, T["h0"], discretization=args.discretization,
+                                   stream=stream)
+            return
         scan.ssm_scan_fwd(T["u"], T["delta"], T["A"], T["B"], T["C"], T["D"], T["z"], T["delta_bias"],
                           case.softplus, T["h0"], layout=case.layout, y=y, h_last=h, workspace=ws, stream=stream,
                           discretization=args.discretization)
@@ -340,11 +359,11 @@ def main():
     elements = case.elements
     value = elements / (ms_per_step * 1e-3)
 
-    slots = algorithmic_slots(case, zoh=args.discretization == "zoh")
+    slots = algorithmic_slots(case, zoh=args.discretization == "zoh", conv_k=args.conv)
     achieved = slots / (launch_ms * 1e-3) / 1e12
     peak = VALU_SLOT_PEAK / 1e12
-    abytes = algorithmic_bytes(case)
-    traffic = load_traffic(args.workload)
+    abytes = algorithmic_bytes(case) + (case.dim * (args.conv + 1) * 4 if args.conv else 0)
+    traffic = load_traffic(args.workload) if not (args.conv or args.discretization != "delta_b") else None
     hbm_gbs = abytes / (launch_ms * 1e-3) / 1e9
 
     line = {
@@ -363,7 +382,7 @@ def main():
         "config": {"workload": args.workload, "layout": case.layout, "io_dtype": case.io_dtype, "batch": case.batch,
                    "seqlen": case.seqlen, "dim": case.dim, "dstate": case.dstate, "nheads": case.nheads,
                    "headdim": case.headdim, "ngroups": case.ngroups, "discretization": args.discretization,
-                   "plan": plan},
+                   "conv_width": args.conv, "plan": plan},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel_ms": launch_ms, "algorithmic_ops_per_launch": slots,
@@ -372,7 +391,9 @@ def main():
                 "frac": hbm_gbs / HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget, zoh=args.discretization == "zoh")
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget, zoh=args.discretization == "zoh",
+                                            conv=None if conv is None else (conv[0].cpu().numpy(),
+                                                                            conv[1].cpu().numpy()))
     print(json.dumps(line), flush=True)
 
 

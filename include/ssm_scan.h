@@ -132,6 +132,37 @@ int ssm_state_update(const void* x, const void* delta, const float* A, const voi
                      const float* D, const void* z, const float* delta_bias, int softplus_flag,
                      const float* h_in, float* h_out, void* y, const ssm_dims_t* dims, void* stream);
 
+/*
+ * Input stage of the Mamba block fused into the scan: the raw input x passes
+ * through a causal depthwise 1-D convolution and SiLU, and the result is the u
+ * of the recurrence (in dt*u and in the D*u skip).  («AI底层架构的一场革命：Mamba如何用
+ * 「状态压缩」挑战Transformer的十年统治», section "Mamba Block：完整模块结构": x_proj ->
+ * 1-D convolution -> SiLU -> S6; «Mamba与SSM状态空间模型：一张摘要卡读完万页档案»,
+ * section "Mamba架构设计".)  The pages give no width: width is 1..4, and
+ *   u_t = SiLU(bias[d] + sum_{j<width} weight[d][j] * x_{t-width+1+j})
+ * where inputs before t = 0 come from state_in (or are 0).
+ */
+typedef struct ssm_conv {
+  const float* weight;  /* (dim, width) float32, required */
+  const float* bias;    /* (dim) float32, or NULL */
+  const float* state_in;/* (batch, dim, width-1) float32: the raw inputs before t = 0, oldest first; or NULL */
+  float* state_out;     /* (batch, dim, width-1) float32: the last width-1 raw inputs; or NULL */
+  int32_t width;        /* 1..4 */
+  int32_t reserved;     /* must be 0 */
+} ssm_conv_t;
+
+/*
+ * ssm_scan_fwd with the input stage above; x has the layout and dtype of u.
+ * Supported for SSM_LAYOUT_BDL with dstate <= 32 (the per-channel kernel);
+ * other shapes return SSM_ERR_UNSUPPORTED.  conv or conv->weight NULL:
+ * SSM_ERR_NULL_ARG; width outside 1..4: SSM_ERR_UNSUPPORTED.  state_out must
+ * not overlap any input or output.  Workspace, stream and errors as for
+ * ssm_scan_fwd (ssm_scan_workspace_size gives the scratch size).
+ */
+int ssm_conv_scan_fwd(const void* x, const ssm_conv_t* conv, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                      const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream);
+
 /* Bytes of scratch ssm_scan_fwd needs for these dims (0 if none); 0 also for invalid dims. */
 size_t ssm_scan_workspace_size(const ssm_dims_t* dims);
 

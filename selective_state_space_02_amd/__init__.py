@@ -7,7 +7,7 @@ Importing this package loads nothing: the library is opened on first use and
 the call fails loudly if it is missing.
 """
 
-__all__ = ["ssm_scan", "ssm_scan_fwd", "ssm_state_update", "library_path"]
+__all__ = ["ssm_scan", "ssm_scan_fwd", "ssm_conv_scan_fwd", "ssm_state_update", "library_path"]
 
 
 def __getattr__(name):

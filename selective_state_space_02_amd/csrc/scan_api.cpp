@@ -182,9 +182,9 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
   return SSM_OK;
 }
 
-int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                 const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                 const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream) {
+static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                      const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream) {
   ssm::g_hip_msg[0] = 0;
   if (!u || !delta || !A || !B || !C || !y || !dims) return SSM_ERR_NULL_ARG;
   ssm::Plan pl;
@@ -193,6 +193,14 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, y, h_last};
   for (const void* q : ptrs)
     if (ssm::misaligned(q)) return SSM_ERR_ALIGN;
+  if (conv) {
+    if (!conv->weight) return SSM_ERR_NULL_ARG;
+    if (conv->width < 1 || conv->width > 4 || conv->reserved != 0) return SSM_ERR_UNSUPPORTED;
+    if (pl.kernel != 1) return SSM_ERR_UNSUPPORTED;   // the fused stage lives in the per-channel kernel
+    const void* cps[] = {conv->weight, conv->bias, conv->state_in, conv->state_out};
+    for (const void* q : cps)
+      if (ssm::misaligned(q)) return SSM_ERR_ALIGN;
+  }
 
   // byte extents for the alias check
   const size_t esz = dims->io_dtype == SSM_BF16 ? 2 : 4;
@@ -213,6 +221,24 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
     if (ssm::overlaps(h_last, n_state, r.p, r.n)) return SSM_ERR_ALIAS;
   }
   if (ssm::overlaps(y, n_x, h_last, n_state)) return SSM_ERR_ALIAS;
+  if (conv && conv->state_out) {
+    const size_t K1 = (size_t)(conv->width - 1);
+    const size_t n_cs = Bn * Dm * K1 * 4, n_w = Dm * (size_t)conv->width * 4;
+    const Range more[] = {{conv->weight, n_w}, {conv->bias, Dm * 4}, {conv->state_in, n_cs}, {y, n_x},
+                          {h_last, n_state}};
+    for (const Range& r : inputs)
+      if (ssm::overlaps(conv->state_out, n_cs, r.p, r.n)) return SSM_ERR_ALIAS;
+    for (const Range& r : more)
+      if (ssm::overlaps(conv->state_out, n_cs, r.p, r.n)) return SSM_ERR_ALIAS;
+  }
+  if (conv) {
+    const Range cin[] = {{conv->weight, Dm * (size_t)conv->width * 4}, {conv->bias, Dm * 4},
+                         {conv->state_in, Bn * Dm * (size_t)(conv->width - 1) * 4}};
+    for (const Range& r : cin) {
+      if (ssm::overlaps(y, n_x, r.p, r.n)) return SSM_ERR_ALIAS;
+      if (ssm::overlaps(h_last, n_state, r.p, r.n)) return SSM_ERR_ALIAS;
+    }
+  }
 
   void* ws = dims->workspace;
   bool own_ws = false;
@@ -250,6 +276,13 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   kp.zsrc = z ? z : u;
   kp.has_z = z ? 1 : 0;
   kp.vec_ok = pl.vec_ok ? 1 : 0;
+  if (conv) {
+    kp.conv_w = conv->weight;
+    kp.conv_b = conv->bias;
+    kp.conv_sin = conv->state_in;
+    kp.conv_sout = conv->state_out;
+    kp.conv_k = conv->width;
+  }
 
   const int he = ssm::launch_plan(pl, kp, stream);
   if (own_ws) {
@@ -264,6 +297,19 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
     return SSM_ERR_HIP;
   }
   return SSM_OK;
+}
+
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                 const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream) {
+  return scan_entry(u, nullptr, delta, A, B, C, D, z, delta_bias, softplus_flag, h0, y, h_last, dims, stream);
+}
+
+int ssm_conv_scan_fwd(const void* x, const ssm_conv_t* conv, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                      const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream) {
+  if (!conv) return SSM_ERR_NULL_ARG;
+  return scan_entry(x, conv, delta, A, B, C, D, z, delta_bias, softplus_flag, h0, y, h_last, dims, stream);
 }
 
 int ssm_state_update(const void* x, const void* delta, const float* A, const void* B, const void* C,

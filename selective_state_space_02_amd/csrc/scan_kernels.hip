@@ -633,8 +633,9 @@ __global__ void __launch_bounds__(256) bc_tile_kernel(KParams p) {
   }
 }
 
-template <typename IO, int NS, int MODE, bool VECOK>
-__global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
+template <typename IO, int NS, int MODE, bool VECOK, bool CONV>
+__global__ void __launch_bounds__(rg::WPG * 64) __attribute__((amdgpu_waves_per_eu((CONV || IO::kBytes == 4) ? 3 : 1)))
+rowgroup_kernel(KParams p) {
   using namespace rg;
   constexpr int kB = IO::kBytes;
   constexpr int NPAD = LPR * NS;
@@ -703,9 +704,55 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
   const float Dd = p.D ? p.D[d] : 0.0f;
   float sum_dt = 0.0f;
 
+  // ---- optional input stage: causal depthwise convolution (width K <= 4) + SiLU
+  // The filter is held right-aligned in 4 taps (leading taps 0), so step t reads the
+  // raw inputs t-3..t.  carry[] holds the 3 raw inputs before the current block; only
+  // lane 7 of a row (the row's last 4 steps) carries them to the next block.
+  float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f, carry[3] = {0.0f, 0.0f, 0.0f};
+  if (CONV) {
+    const int K = p.conv_k;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j >= 4 - K) cw[j] = p.conv_w[(int64_t)d * K + j - (4 - K)];
+    cb = p.conv_b ? p.conv_b[d] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int64_t t = t_seg0 - 3 + i;
+      if (t >= 0) {
+        carry[i] = IO::cvt(IO::ld_bits(pu, (int64_t)row_e * L + t));
+      } else if (p.conv_sin && t >= -(int64_t)(K - 1)) {      // inputs before t = 0: the carried state
+        carry[i] = p.conv_sin[((int64_t)b * p.dim + d) * (K - 1) + (K - 1) + t];
+      }
+    }
+  }
+
   // --------------------------------------------------------- one time block
-  // raw/uu/zz: delta/u/z of steps 4k..4k+3 (fp32); the block's B/C tile is already in LDS
-  auto run_block = [&](int64_t tb, int nvalid, const float (&raw)[4], const float (&uu)[4], const float (&zz)[4]) {
+  // raw/uin/zz: delta/u/z of steps 4k..4k+3 (fp32); the block's B/C tile is already in LDS
+  auto run_block = [&](int64_t tb, int nvalid, const float (&raw)[4], const float (&uin)[4], const float (&zz)[4]) {
+    float uu[4];
+    if (CONV) {
+      // raw inputs of the 3 steps before this lane's first: lane k-1's last 3, or the carry
+      float xw[7];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const float from_left = __shfl(uin[1 + i], lane > 0 ? lane - 1 : 0);
+        const float from_carry = __shfl(carry[i], (lane & ~(LPR - 1)) + LPR - 1);
+        xw[i] = k == 0 ? from_carry : from_left;
+        carry[i] = uin[1 + i];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xw[3 + q] = uin[q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float c = cb;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) c = fmaf(cw[m], xw[q + m], c);
+        uu[q] = silu_f(c);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) uu[q] = uin[q];
+    }
     // prologue: step sizes and dt*u of this lane's 4 steps
     float dtv[4], duv[4];
 #pragma unroll
@@ -890,11 +937,23 @@ __global__ void __launch_bounds__(rg::WPG * 64) rowgroup_kernel(KParams p) {
         p.wsH[i] = h[j];
       }
     }
-  } else if (p.h_last && row_ok && seg == p.nseg - 1) {
+  } else if (row_ok && seg == p.nseg - 1) {
+    if (p.h_last) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int n = k * NS + j;
-      if (n < p.N) p.h_last[((int64_t)b * p.dim + d) * p.N + n] = h[j];
+      for (int j = 0; j < NS; ++j) {
+        const int n = k * NS + j;
+        if (n < p.N) p.h_last[((int64_t)b * p.dim + d) * p.N + n] = h[j];
+      }
+    }
+    if (CONV && p.conv_sout && k == 0) {   // the last K-1 raw inputs, for a continuing call
+      const int K = p.conv_k;
+      for (int j = 0; j < K - 1; ++j) {
+        const int64_t t = L - (K - 1) + j;
+        float v = 0.0f;
+        if (t >= 0) v = IO::cvt(IO::ld_bits(pu, (int64_t)row_e * L + t));
+        else if (p.conv_sin) v = p.conv_sin[((int64_t)b * p.dim + d) * (K - 1) + (K - 1) + t];
+        p.conv_sout[((int64_t)b * p.dim + d) * (K - 1) + j] = v;
+      }
     }
   }
 }
@@ -921,7 +980,7 @@ int launch_variant(const Plan& pl, const KParams& kp, hipStream_t st) {
   return launch_modes<LAYOUT, IO, NS, NW, TB, false>(pl, kp, st);
 }
 
-template <typename IO, int NS, bool VECOK>
+template <typename IO, int NS, bool VECOK, bool CONV>
 int launch_rowgroup_modes(const Plan& pl, const KParams& kp, hipStream_t st) {
   const dim3 block(rg::WPG * 64);
   const int total = kp.blocks_per_group * kp.G;
@@ -932,18 +991,23 @@ int launch_rowgroup_modes(const Plan& pl, const KParams& kp, hipStream_t st) {
     if (e != hipSuccess) return (int)e;
   }
   if (pl.nseg > 1) {
-    hipLaunchKernelGGL((rowgroup_kernel<IO, NS, 1, VECOK>), dim3(gx, kp.batch, pl.nseg - 1), block, 0, st, kp);
+    hipLaunchKernelGGL((rowgroup_kernel<IO, NS, 1, VECOK, CONV>), dim3(gx, kp.batch, pl.nseg - 1), block, 0, st,
+                       kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
-  hipLaunchKernelGGL((rowgroup_kernel<IO, NS, 0, VECOK>), dim3(gx, kp.batch, pl.nseg), block, 0, st, kp);
+  hipLaunchKernelGGL((rowgroup_kernel<IO, NS, 0, VECOK, CONV>), dim3(gx, kp.batch, pl.nseg), block, 0, st, kp);
   return (int)hipGetLastError();
 }
 
 template <typename IO, int NS>
 int launch_rowgroup(const Plan& pl, const KParams& kp, hipStream_t st) {
-  if (kp.L % 4 == 0) return launch_rowgroup_modes<IO, NS, true>(pl, kp, st);
-  return launch_rowgroup_modes<IO, NS, false>(pl, kp, st);
+  if (kp.conv_k > 0) {
+    if (kp.L % 4 == 0) return launch_rowgroup_modes<IO, NS, true, true>(pl, kp, st);
+    return launch_rowgroup_modes<IO, NS, false, true>(pl, kp, st);
+  }
+  if (kp.L % 4 == 0) return launch_rowgroup_modes<IO, NS, true, false>(pl, kp, st);
+  return launch_rowgroup_modes<IO, NS, false, false>(pl, kp, st);
 }
 
 template <int LAYOUT, typename IO>

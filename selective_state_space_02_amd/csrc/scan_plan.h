@@ -47,6 +47,11 @@ struct KParams {
   float* wsP;   // [seg][b][n][d] decay product of each aggregated segment
   float* wsH;   // [seg][b][n][d] zero-start end state of each aggregated segment
   float* bct;   // row-group kernel: [b][g][block] B/C tiles in LDS order (bc_tile_kernel)
+  const float* conv_w;     // optional input stage (row-group kernel): (dim, conv_k) filters
+  const float* conv_b;     // (dim) or NULL
+  const float* conv_sin;   // (batch, dim, conv_k-1) raw inputs before t = 0, or NULL (zeros)
+  float* conv_sout;        // (batch, dim, conv_k-1) last raw inputs, or NULL
+  int conv_k;              // 0: no input stage; 1..4: filter width
   int64_t nblk; // row-group kernel: time blocks per sequence
   int64_t L, seg_len;
   int batch, dim, N, Npad, H, P, G;

@@ -34,7 +34,7 @@ SSM_ERR_WORKSPACE = -6
 SSM_ERR_HIP = -7
 
 EXPORTED = ("ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_strerror", "ssm_scan_describe", "ssm_scan_version",
-            "ssm_state_update")
+            "ssm_state_update", "ssm_conv_scan_fwd")
 
 
 class Dims(ctypes.Structure):
@@ -51,6 +51,17 @@ class Dims(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("discretization", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class Conv(ctypes.Structure):
+    _fields_ = [
+        ("weight", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("state_in", ctypes.c_void_p),
+        ("state_out", ctypes.c_void_p),
+        ("width", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -81,6 +92,9 @@ def load_library():
         lib.ssm_scan_describe.argtypes = [ctypes.POINTER(Dims), ctypes.c_char_p, ctypes.c_size_t]
         lib.ssm_scan_version.restype = ctypes.c_int
         lib.ssm_scan_version.argtypes = []
+        lib.ssm_conv_scan_fwd.restype = ctypes.c_int
+        lib.ssm_conv_scan_fwd.argtypes = [vp, ctypes.POINTER(Conv), vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                                          vp, vp, ctypes.POINTER(Dims), vp]
         lib.ssm_state_update.restype = ctypes.c_int
         lib.ssm_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                          ctypes.POINTER(Dims), vp]
@@ -261,3 +275,59 @@ def ssm_state_update(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: t
     if rc != SSM_OK:
         raise RuntimeError(f"ssm_state_update failed ({rc}): {strerror(rc)}")
     return y, h_out
+
+
+def call_conv_raw(x, conv: Conv, delta, A, B, C, D, z, delta_bias, softplus, h0, y, h_last, dims: Dims,
+                  stream=None) -> int:
+    """Direct ABI call of ssm_conv_scan_fwd with integer addresses (None = NULL)."""
+    return int(load_library().ssm_conv_scan_fwd(x, None if conv is None else ctypes.byref(conv), delta, A, B, C, D,
+                                               z, delta_bias, int(bool(softplus)), h0, y, h_last, ctypes.byref(dims),
+                                               stream))
+
+
+def ssm_conv_scan_fwd(x: torch.Tensor, conv_weight: torch.Tensor, conv_bias: Optional[torch.Tensor],
+                      delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                      D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                      delta_bias: Optional[torch.Tensor] = None, softplus: bool = True,
+                      h0: Optional[torch.Tensor] = None, *, conv_state_in: Optional[torch.Tensor] = None,
+                      want_conv_state: bool = False, discretization: str = "delta_b",
+                      stream: Optional[torch.cuda.Stream] = None):
+    """Causal depthwise conv1d + SiLU on x, then the scan ((B, D, L) layout).  conv_weight (D, K) float32,
+    K in 1..4.  Returns (y, h_last, conv_state_out or None)."""
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssm_conv_scan_fwd runs on the GPU: tensors must be on a cuda device")
+    Bsz, Dm, L = x.shape
+    K = conv_weight.shape[1]
+    f32 = torch.float32
+    _check(conv_weight, "conv_weight", f32, (Dm, K), dev)
+    _check(conv_bias, "conv_bias", f32, (Dm,), dev)
+    _check(conv_state_in, "conv_state_in", f32, (Bsz, Dm, K - 1), dev)
+    io = x.dtype
+    G, N = B.shape[1], B.shape[2]
+    for t, name, dt, shp in ((delta, "delta", io, (Bsz, Dm, L)), (A, "A", f32, (Dm, N)), (B, "B", io, (Bsz, G, N, L)),
+                             (C, "C", io, (Bsz, G, N, L)), (D, "D", f32, (Dm,)), (z, "z", io, (Bsz, Dm, L)),
+                             (delta_bias, "delta_bias", f32, (Dm,)), (h0, "h0", f32, (Bsz, Dm, N))):
+        _check(t, name, dt, shp, dev)
+    y = torch.empty_like(x)
+    h_last = torch.empty((Bsz, Dm, N), dtype=f32, device=dev)
+    state_out = torch.empty((Bsz, Dm, max(K - 1, 1)), dtype=f32, device=dev) if want_conv_state else None
+    dims = make_dims("bdl", "bf16" if io == torch.bfloat16 else "f32", Bsz, L, Dm, N, 0, 0, G, discretization)
+    need = int(lib.ssm_scan_workspace_size(ctypes.byref(dims)))
+    ws = None
+    if need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        dims.workspace = ws.data_ptr()
+        dims.workspace_bytes = need
+    conv = Conv(conv_weight.data_ptr(), _ptr(conv_bias), _ptr(conv_state_in),
+                None if state_out is None else state_out.data_ptr(), K, 0)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.ssm_conv_scan_fwd(_ptr(x), ctypes.byref(conv), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                               _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(h0), _ptr(y), _ptr(h_last),
+                               ctypes.byref(dims), ctypes.c_void_p(st.cuda_stream))
+    if rc != SSM_OK:
+        raise RuntimeError(f"ssm_conv_scan_fwd failed ({rc}): {strerror(rc)}")
+    if state_out is not None and K == 1:
+        state_out = state_out[:, :, :0]
+    return y, h_last, state_out

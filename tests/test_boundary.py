@@ -191,3 +191,29 @@ def test_discretization_field():
     bad = dims(seqlen=1)
     bad.reserved = 1
     assert call_update(bad) == scan.SSM_ERR_UNSUPPORTED
+
+
+def test_conv_scan_rejects_bad_arguments():
+    def cv(**kw):
+        a = dict(weight=P["A"], bias=P["D"], state_in=None, state_out=None, width=4, reserved=0)
+        a.update(kw)
+        return scan.Conv(a["weight"], a["bias"], a["state_in"], a["state_out"], a["width"], a["reserved"])
+
+    def callc(conv, dm=None, **over):
+        a = dict(P)
+        a.update(over)
+        return scan.call_conv_raw(a["u"], conv, a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], True,
+                                  a["h0"], a["y"], a["h_last"], dm or dims())
+
+    assert callc(None) == scan.SSM_ERR_NULL_ARG
+    assert callc(cv(weight=None)) == scan.SSM_ERR_NULL_ARG
+    assert callc(cv(width=0)) == scan.SSM_ERR_UNSUPPORTED
+    assert callc(cv(width=5)) == scan.SSM_ERR_UNSUPPORTED
+    assert callc(cv(reserved=1)) == scan.SSM_ERR_UNSUPPORTED
+    assert callc(cv(), dims(dstate=64)) == scan.SSM_ERR_UNSUPPORTED                      # workgroup-kernel shape
+    assert callc(cv(), scan.make_dims("blhp", "bf16", 2, 64, 128, 16, nheads=2, headdim=64)) == \
+        scan.SSM_ERR_UNSUPPORTED
+    assert callc(cv(state_in=P["ws"] + 4)) == scan.SSM_ERR_ALIGN
+    assert callc(cv(state_out=P["u"])) == scan.SSM_ERR_ALIAS
+    assert callc(cv(state_out=P["y"] + 16)) == scan.SSM_ERR_ALIAS
+    assert callc(cv(state_in=P["ws"]), y=P["ws"] + 16) == scan.SSM_ERR_ALIAS
