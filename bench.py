@@ -73,7 +73,8 @@ def algorithmic_bytes(case) -> int:
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in ("selective_state_space_02_amd/csrc/scan_kernels.hip", "selective_state_space_02_amd/csrc/scan_api.cpp",
-              "selective_state_space_02_amd/csrc/scan_plan.h", "selective_state_space_02_amd/csrc/update_kernels.hip"):
+              "selective_state_space_02_amd/csrc/scan_plan.h", "selective_state_space_02_amd/csrc/update_kernels.hip",
+              "selective_state_space_02_amd/csrc/ssd_kernels.hip"):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 

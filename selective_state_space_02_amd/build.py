@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssm_scan.so")
 SOURCES = [os.path.join(CSRC, "scan_api.cpp"), os.path.join(CSRC, "scan_kernels.hip"),
-           os.path.join(CSRC, "update_kernels.hip")]
+           os.path.join(CSRC, "update_kernels.hip"), os.path.join(CSRC, "ssd_kernels.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

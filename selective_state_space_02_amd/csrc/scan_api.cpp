@@ -119,6 +119,23 @@ int make_plan(const ssm_dims_t* d, Plan* pl) {
     target = 2 * kCUs;
   }
   if ((int64_t)p.grid_rows > 0x7fffffff) return SSM_ERR_BAD_DIMS;
+  // Multi-head layout in bfloat16 with 32/64/128 states: the chunked form on MFMA
+  // (SSM_SCAN_SSD=0 keeps the scan kernel).
+  const char* ssd_env = std::getenv("SSM_SCAN_SSD");
+  const bool ssd_ok = !(ssd_env && *ssd_env == '0');
+  if (ssd_ok && d->layout == SSM_LAYOUT_BLHP && d->io_dtype == SSM_BF16 && (N == 32 || N == 64 || N == 128) &&
+      d->headdim % 32 == 0 && d->nheads <= 65535) {
+    p.kernel = 2;
+    p.ps = d->headdim % 64 == 0 ? 64 : 32;
+    p.NS = 0; p.NW = 4; p.TB = 64;
+    p.grid_rows = (int)(d->headdim / p.ps);
+    p.nseg = 1;
+    p.seg_len = d->seqlen;
+    p.vec_ok = true;
+    p.seg_bytes = p.bc_bytes = p.ws_bytes = 0;
+    *pl = p;
+    return SSM_OK;
+  }
   p.nseg = choose_segments(d->seqlen, units, target, p.TB, &p.seg_len);
   p.vec_ok = (d->layout == SSM_LAYOUT_BDL) && (d->seqlen % 4 == 0);
   p.seg_bytes = p.nseg > 1 ? (size_t)2 * (size_t)(p.nseg - 1) * (size_t)d->batch * (size_t)p.Npad *
@@ -137,6 +154,7 @@ int make_plan(const ssm_dims_t* d, Plan* pl) {
 }
 
 int launch_plan(const Plan& plan, const KParams& kp, void* stream) {
+  if (plan.kernel == 2) return launch_ssd(kp, plan.ps, plan.disc == SSM_DISC_ZOH, stream);
   return plan.disc == SSM_DISC_ZOH ? launch_plan_zoh(plan, kp, stream) : launch_plan_delta_b(plan, kp, stream);
 }
 
@@ -174,7 +192,8 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
     std::snprintf(buf, buf_len,
                   "kernel=%s layout=%s io=%s disc=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d "
                   "ws=%zu",
-                  p.kernel == 1 ? "rowgroup" : "workgroup", p.layout == SSM_LAYOUT_BDL ? "bdl" : "blhp",
+                  p.kernel == 2 ? "ssd" : p.kernel == 1 ? "rowgroup" : "workgroup",
+                  p.layout == SSM_LAYOUT_BDL ? "bdl" : "blhp",
                   p.io == SSM_BF16 ? "bf16" : "f32", p.disc == SSM_DISC_ZOH ? "zoh" : "delta_b", p.NS, p.NW, p.TB,
                   p.Npad, p.grid_rows, (long long)dims->batch, p.nseg, (long long)p.seg_len, (int)p.vec_ok,
                   p.ws_bytes);

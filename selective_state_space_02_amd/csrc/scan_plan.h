@@ -16,7 +16,9 @@
 namespace ssm {
 
 struct Plan {
-  int kernel = 0;            // 0: workgroup kernel (64 rows, states over waves); 1: row-group kernel
+  int kernel = 0;            // 0: workgroup kernel (64 rows, states over waves); 1: row-group kernel;
+                             // 2: chunked multi-head kernel on MFMA (ssd_kernels.hip)
+  int ps = 0;                // kernel 2: positions per workgroup
   int disc = 0;              // SSM_DISC_DELTA_B or SSM_DISC_ZOH
   int layout = 0, io = 0;
   int NS = 0, NW = 0, TB = 0, Npad = 0;
@@ -93,6 +95,9 @@ int make_plan(const ssm_dims_t* d, Plan* plan);
 int launch_plan(const Plan& plan, const KParams& kp, void* stream);
 int launch_plan_delta_b(const Plan& plan, const KParams& kp, void* stream);
 int launch_plan_zoh(const Plan& plan, const KParams& kp, void* stream);
+
+// Enqueue the chunked multi-head kernel (bf16 storage, N in {32,64,128}, ps in {32,64} dividing P).
+int launch_ssd(const KParams& kp, int ps, int zoh, void* stream);
 
 // Enqueue the state-update kernel.  Returns a hipError_t value (0 = success).
 int launch_update(const UParams& p, int layout, int io, int Npad, void* stream);

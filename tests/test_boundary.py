@@ -133,7 +133,11 @@ def test_workspace_size_and_plan():
     d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # 40 row blocks: segmented
     assert scan.workspace_size(d4) > 0
     d5 = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
-    assert "kernel=workgroup" in scan.describe(d5) and "NS=16" in scan.describe(d5)
+    assert "kernel=ssd" in scan.describe(d5) and scan.workspace_size(d5) == 0
+    d5f = scan.make_dims("blhp", "f32", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
+    assert "kernel=workgroup" in scan.describe(d5f) and "NS=16" in scan.describe(d5f)
+    d5n = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 100, nheads=80, headdim=64, ngroups=1)
+    assert "kernel=workgroup" in scan.describe(d5n)
     bad = dims(dim=0)
     assert scan.workspace_size(bad) == 0
     with pytest.raises(ValueError):
@@ -217,3 +221,9 @@ def test_conv_scan_rejects_bad_arguments():
     assert callc(cv(state_out=P["u"])) == scan.SSM_ERR_ALIAS
     assert callc(cv(state_out=P["y"] + 16)) == scan.SSM_ERR_ALIAS
     assert callc(cv(state_in=P["ws"]), y=P["ws"] + 16) == scan.SSM_ERR_ALIAS
+
+
+def test_ssd_override_env(monkeypatch):
+    d5 = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
+    monkeypatch.setenv("SSM_SCAN_SSD", "0")
+    assert "kernel=workgroup" in scan.describe(d5)
