@@ -63,7 +63,7 @@ bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u); }
 
 }  // namespace
 
-int make_plan(const ssm_dims_t* d, Plan* pl) {
+int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
   if (!d || !pl) return SSM_ERR_NULL_ARG;
   if (d->layout != SSM_LAYOUT_BDL && d->layout != SSM_LAYOUT_BLHP) return SSM_ERR_UNSUPPORTED;
   if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
@@ -147,6 +147,25 @@ int make_plan(const ssm_dims_t* d, Plan* pl) {
     p.bc_bytes = (size_t)d->batch * (size_t)d->ngroups * (size_t)p.nblk * (size_t)p.TB * 2 * (size_t)p.Npad *
                  sizeof(float);
     p.bc_bytes = (p.bc_bytes + 255) & ~(size_t)255;
+    // 16 states in one segment: the mixed launch (80 channels per workgroup, one
+    // workgroup per CU, the same work on every SIMD) when its busiest SIMD has less
+    // to do than the plain launch's.  A workgroup costs about 2.6 plain waves of
+    // work per SIMD.  SSM_SCAN_MIXED=0/1 forces the choice (tests, tuning).
+    if (allow_mixed && p.Npad == 16 && p.nseg == 1) {
+      const int64_t mixed_blocks = (rows_per_group + 79) / 80;
+      const int64_t wgs = mixed_blocks * groups_or_heads * d->batch;
+      const int64_t waves = (int64_t)p.blocks_per_group * groups_or_heads * d->batch;
+      const double cost_mixed = 2.6 * (double)((wgs + kCUs - 1) / kCUs);
+      const double cost_plain = (double)((waves + 4 * kCUs - 1) / (4 * kCUs));
+      bool mixed = cost_mixed < cost_plain;
+      const char* env = std::getenv("SSM_SCAN_MIXED");
+      if (env && *env) mixed = *env != '0';
+      if (mixed && groups_or_heads * mixed_blocks <= 0x7fffffff) {
+        p.kernel = 3;
+        p.blocks_per_group = (int)mixed_blocks;
+        p.grid_rows = (int)(groups_or_heads * mixed_blocks);
+      }
+    }
   }
   p.ws_bytes = p.bc_bytes + p.seg_bytes;
   *pl = p;
@@ -192,7 +211,7 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
     std::snprintf(buf, buf_len,
                   "kernel=%s layout=%s io=%s disc=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d "
                   "ws=%zu",
-                  p.kernel == 2 ? "ssd" : p.kernel == 1 ? "rowgroup" : "workgroup",
+                  p.kernel == 3 ? "rowgroup_mixed" : p.kernel == 2 ? "ssd" : p.kernel == 1 ? "rowgroup" : "workgroup",
                   p.layout == SSM_LAYOUT_BDL ? "bdl" : "blhp",
                   p.io == SSM_BF16 ? "bf16" : "f32", p.disc == SSM_DISC_ZOH ? "zoh" : "delta_b", p.NS, p.NW, p.TB,
                   p.Npad, p.grid_rows, (long long)dims->batch, p.nseg, (long long)p.seg_len, (int)p.vec_ok,
@@ -207,7 +226,7 @@ static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, 
   ssm::g_hip_msg[0] = 0;
   if (!u || !delta || !A || !B || !C || !y || !dims) return SSM_ERR_NULL_ARG;
   ssm::Plan pl;
-  int rc = ssm::make_plan(dims, &pl);
+  int rc = ssm::make_plan(dims, &pl, conv == nullptr);   // the fused input stage runs in the plain launch
   if (rc != SSM_OK) return rc;
   const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, y, h_last};
   for (const void* q : ptrs)

@@ -62,6 +62,7 @@ __device__ __forceinline__ float zoh_factor(float y, float a) {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- element I/O
 // Global loads are issued as raw bits one time block ahead (so their latency hides
@@ -96,10 +97,15 @@ struct F32IO {
     if constexpr (V == 2) *(float2*)((float*)p + i) = make_float2(v[0], v[1]);
     if constexpr (V == 4) *(float4*)((float*)p + i) = make_float4(v[0], v[1], v[2], v[3]);
   }
-  // 4 consecutive outputs with a streaming (nontemporal) store: written once, never re-read
-  __device__ static void stv4_stream(void* p, const float* v) {
-    const f32x4 w = {v[0], v[1], v[2], v[3]};
-    __builtin_nontemporal_store(w, (f32x4*)p);
+  // V consecutive outputs with a streaming (nontemporal) store: written once, never re-read
+  template <int V> __device__ static void stv_stream(void* p, const float* v) {
+    if constexpr (V == 4) {
+      const f32x4 w = {v[0], v[1], v[2], v[3]};
+      __builtin_nontemporal_store(w, (f32x4*)p);
+    } else {
+      const f32x2 w = {v[0], v[1]};
+      __builtin_nontemporal_store(w, (f32x2*)p);
+    }
   }
 };
 
@@ -145,11 +151,15 @@ struct BF16IO {
       *(uint2*)((uint16_t*)p + i) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c));
     }
   }
-  __device__ static void stv4_stream(void* p, const float* v) {
+  template <int V> __device__ static void stv_stream(void* p, const float* v) {
     const bf16x2 a = {(__bf16)v[0], (__bf16)v[1]};
-    const bf16x2 c = {(__bf16)v[2], (__bf16)v[3]};
-    const u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
-    __builtin_nontemporal_store(w, (u32x2*)p);
+    if constexpr (V == 4) {
+      const bf16x2 c = {(__bf16)v[2], (__bf16)v[3]};
+      const u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
+      __builtin_nontemporal_store(w, (u32x2*)p);
+    } else {
+      __builtin_nontemporal_store(__builtin_bit_cast(uint32_t, a), (uint32_t*)p);
+    }
   }
 };
 
@@ -580,24 +590,33 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
 }
 
 // ------------------------------------------------- row-group kernel ((B,D,L), N <= 32)
-// One wave owns 8 rows (channels of one batch item and channel group) and their
-// whole state vector: 8 lanes per row, NS states per lane.  Waves never wait for
-// each other: there is no workgroup barrier.  A time block is 32 steps; lane k of a
-// row loads, prepares (step size, dt*u) and finishes (readout sum, D*u, gate, store)
-// steps 4k..4k+3 of its row, and shares the prepared values with the other lanes of
-// the row through a per-wave LDS tile.  B_t/C_t of the block come from a tile that
-// bc_tile_kernel has already converted to fp32 in the LDS order, so staging them is
-// a straight copy.  The readout partial sums of the 8 lanes of a row are combined
-// through LDS.  u/delta/z/y are addressed as a wave-uniform row base plus a 32-bit
-// lane offset.  Full blocks use vector loads issued one block ahead; the ragged last
-// block of a segment is loaded element by element after the main loop.
+// One wave owns a group of channels of one batch item and channel group and their
+// whole state vectors: LPR lanes per channel (8 or 16), NS = N_pad/LPR states per lane.
+// Waves never wait for each other: there is no workgroup barrier.  A time block is 32
+// steps; lane k of a channel loads, prepares (step size, dt*u) and finishes (readout
+// sum, D*u, gate, store) steps QPL*k .. QPL*k+QPL-1 of its channel (QPL = 32/LPR) and
+// shares the prepared values with the channel's other lanes through a per-wave LDS
+// tile.  B_t/C_t of the block come from a tile that bc_tile_kernel has already
+// converted to fp32 in the LDS order ([t][n][B C]), so staging is a straight copy.
+// The readout partial sums of a channel's lanes are combined through LDS.
+// u/delta/z/y are addressed as a wave-uniform row base plus a 32-bit lane offset.
+// Full blocks use vector loads issued one block ahead; the ragged last block of a
+// segment is loaded element by element after the main loop.
+//
+// Two launches use the same wave body: the plain one (waves of 8 lanes per channel),
+// and a mixed one for 16 states whose workgroup is 8 waves of 8 lanes per channel
+// plus 4 waves of 16 lanes per channel (80 channels).  The hardware places wave w of a
+// workgroup on the same SIMD as wave w+4, so every SIMD gets two 8-channel waves and
+// one 4-channel wave: equal work per SIMD when the channel count is a multiple of
+// 80 x 256 (the plain launch would leave 3 waves on half the SIMDs and 2 on the rest).
 namespace rg {
-constexpr int LPR = 8;          // lanes per row
-constexpr int RPW = 64 / LPR;   // rows per wave
-constexpr int TB = 4 * LPR;     // steps per block (4 per lane)
+constexpr int TB = 32;          // steps per block
 constexpr int TP = TB + 4;      // padded LDS row stride
-constexpr int WPG = 4;          // waves per workgroup (independent; packing only)
-template <int NS> constexpr int bc_tile() { return TB * 2 * LPR * NS; }   // floats per B/C tile
+constexpr int WPG = 4;          // waves per workgroup of the plain launch (independent; packing only)
+constexpr int MIX_WAVES = 12;   // mixed launch: 8 waves of 8 lanes per channel, then 4 of 16
+constexpr int MIX_ROWS = 80;    // channels per mixed workgroup
+constexpr int TILE = 64 * TP;   // dt|du tile, later the partial sums (one row of TP per lane)
+template <int NPAD> constexpr int bc_tile() { return TB * 2 * NPAD; }   // floats per B/C tile
 }  // namespace rg
 
 // order the wave's own LDS writes before its reads of other lanes' data
@@ -608,16 +627,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // B_t, C_t of one (batch item, group, time block) as the tile the row-group kernel
-// copies into LDS: [t (32)][k (8)][B of states k*NS..k*NS+NS-1, then C of them],
-// fp32, zero for states >= N and steps >= L.  Grid (time blocks, G, batch).
-template <typename IO, int NS>
+// copies into LDS: [t (32)][n (N_pad)][B C], fp32, zero for states >= N and steps >= L.
+// Grid (time blocks, G, batch).
+template <typename IO, int NPAD>
 __global__ void __launch_bounds__(256) bc_tile_kernel(KParams p) {
   using namespace rg;
-  constexpr int NPAD = LPR * NS;
-  constexpr int TILE = bc_tile<NS>();
+  constexpr int TILE_BC = bc_tile<NPAD>();
   const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int64_t t0 = (int64_t)blk * TB;
-  float* dst = p.bct + ((int64_t)(b * p.G + g) * p.nblk + blk) * TILE;
+  float* dst = p.bct + ((int64_t)(b * p.G + g) * p.nblk + blk) * TILE_BC;
   const int64_t src_row = ((int64_t)b * p.G + g) * p.N;
   for (int i = threadIdx.x; i < NPAD * TB; i += 256) {
     const int n = i / TB, t = i % TB;                 // consecutive threads walk time: coalesced reads
@@ -627,43 +645,36 @@ __global__ void __launch_bounds__(256) bc_tile_kernel(KParams p) {
       bv = IO::cvt(IO::ld_bits(p.B, s));
       cv = IO::cvt(IO::ld_bits(p.C, s));
     }
-    float* o = dst + t * 2 * NPAD + (n / NS) * 2 * NS + n % NS;
-    o[0] = bv;
-    o[NS] = cv;
+    *(float2*)(dst + (t * NPAD + n) * 2) = make_float2(bv, cv);
   }
 }
 
-template <typename IO, int NS, int MODE, bool VECOK, bool CONV>
-__global__ void __launch_bounds__(rg::WPG * 64) __attribute__((amdgpu_waves_per_eu((CONV || IO::kBytes == 4) ? 3 : 1)))
-rowgroup_kernel(KParams p) {
+// The body of one wave: channels r0 .. r0+64/LPR-1 of group g (clamped at the group's end).
+template <typename IO, int LPR, int NS, int MODE, bool VECOK, bool CONV>
+__device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, float* s_tile, float* s_bc) {
   using namespace rg;
+  constexpr int RPW = 64 / LPR;                              // channels per wave
+  constexpr int QPL = TB / LPR;                              // steps per lane in prologue/epilogue
   constexpr int kB = IO::kBytes;
   constexpr int NPAD = LPR * NS;
-  constexpr int TILE_BC = bc_tile<NS>();
+  constexpr int TILE_BC = bc_tile<NPAD>();
   constexpr int NQ = TILE_BC / (64 * 4);                     // float4 of the B/C tile per lane
-  using Raw4 = typename RawT<4 * kB>::T;                     // 4 steps of one tensor
-  constexpr int TILE = (RPW * LPR * TP > 2 * RPW * TP) ? RPW * LPR * TP : 2 * RPW * TP;
+  using RawQ = typename RawT<QPL * kB>::T;                   // QPL steps of one tensor
+  static_assert(QPL == 4 || QPL == 2, "8 or 16 lanes per channel");
+  static_assert(!CONV || QPL == 4, "the input stage needs 4 steps per lane");
 
-  __shared__ __attribute__((aligned(16))) float s_tile[WPG][TILE];        // dt|du, later partial sums
-  __shared__ __attribute__((aligned(16))) float s_bc[WPG][TILE_BC];       // [t][k][B(NS) C(NS)]
-
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int row = lane / LPR, k = lane % LPR;
-  const int rb = blockIdx.x * WPG + wv;
-  if (rb >= p.blocks_per_group * p.G) return;               // no barriers: idle waves may leave
-  float* const s_dt = &s_tile[wv][0];
-  float* const s_du = &s_tile[wv][RPW * TP];
-  float* const s_part = &s_tile[wv][0];
-  float* const s_b = &s_bc[wv][0];
+  float* const s_dt = s_tile;
+  float* const s_du = s_tile + RPW * TP;
+  float* const s_part = s_tile;
+  float* const s_b = s_bc;
 
   const int b = blockIdx.y;
   const int seg = blockIdx.z;
   const int64_t L = p.L;
   const int64_t t_seg0 = (int64_t)seg * p.seg_len;
   const int64_t t_seg1 = min(L, t_seg0 + p.seg_len);
-  const int g = rb / p.blocks_per_group;
-  const int r0 = (rb % p.blocks_per_group) * RPW;
   const int rows_in = min(RPW, p.rows_per_group - r0);
   const bool row_ok = row < rows_in;
   // Lanes of rows past the end of the group compute row 0 of the wave again (same
@@ -679,7 +690,7 @@ rowgroup_kernel(KParams p) {
   const char* const pdl = (const char*)p.delta + base;
   const char* const pz = (const char*)p.zsrc + base;
   char* const py = (char*)p.y + base;
-  const uint32_t loff = ((uint32_t)row_e * (uint32_t)L + 4u * (uint32_t)k) * kB;
+  const uint32_t loff = ((uint32_t)row_e * (uint32_t)L + (uint32_t)(QPL * k)) * kB;
   const f32x4* const tiles = (const f32x4*)(p.bct + (int64_t)(b * p.G + g) * p.nblk * TILE_BC);
 
   // ---- states n = k*NS + j of channel d
@@ -707,7 +718,7 @@ rowgroup_kernel(KParams p) {
   // ---- optional input stage: causal depthwise convolution (width K <= 4) + SiLU
   // The filter is held right-aligned in 4 taps (leading taps 0), so step t reads the
   // raw inputs t-3..t.  carry[] holds the 3 raw inputs before the current block; only
-  // lane 7 of a row (the row's last 4 steps) carries them to the next block.
+  // the row's last lane (the row's last 4 steps) carries them to the next block.
   float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f, carry[3] = {0.0f, 0.0f, 0.0f};
   if (CONV) {
     const int K = p.conv_k;
@@ -727,10 +738,11 @@ rowgroup_kernel(KParams p) {
   }
 
   // --------------------------------------------------------- one time block
-  // raw/uin/zz: delta/u/z of steps 4k..4k+3 (fp32); the block's B/C tile is already in LDS
-  auto run_block = [&](int64_t tb, int nvalid, const float (&raw)[4], const float (&uin)[4], const float (&zz)[4]) {
-    float uu[4];
-    if (CONV) {
+  // raw/uin/zz: delta/u/z of this lane's QPL steps (fp32); the block's B/C tile is in LDS
+  auto run_block = [&](int64_t tb, int nvalid, const float (&raw)[QPL], const float (&uin)[QPL],
+                       const float (&zz)[QPL]) {
+    float uu[QPL];
+    if constexpr (CONV) {
       // raw inputs of the 3 steps before this lane's first: lane k-1's last 3, or the carry
       float xw[7];
 #pragma unroll
@@ -751,21 +763,26 @@ rowgroup_kernel(KParams p) {
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) uu[q] = uin[q];
+      for (int q = 0; q < QPL; ++q) uu[q] = uin[q];
     }
-    // prologue: step sizes and dt*u of this lane's 4 steps
-    float dtv[4], duv[4];
+    // prologue: step sizes and dt*u of this lane's steps
+    float dtv[QPL], duv[QPL];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool ok = 4 * k + q < nvalid;
+    for (int q = 0; q < QPL; ++q) {
+      const bool ok = QPL * k + q < nvalid;
       const float rr = raw[q] + bias;
-      const float sp = softplus_f(rr);                        // branch-free: the 4 steps interleave
+      const float sp = softplus_f(rr);                        // branch-free: the steps interleave
       const float dt = ok ? (p.softplus ? sp : rr) : 0.0f;
       dtv[q] = dt;
       duv[q] = dt * uu[q];
     }
-    *(float4*)&s_dt[row * TP + 4 * k] = make_float4(dtv[0], dtv[1], dtv[2], dtv[3]);
-    *(float4*)&s_du[row * TP + 4 * k] = make_float4(duv[0], duv[1], duv[2], duv[3]);
+    if constexpr (QPL == 4) {
+      *(float4*)&s_dt[row * TP + 4 * k] = make_float4(dtv[0], dtv[1], dtv[2], dtv[3]);
+      *(float4*)&s_du[row * TP + 4 * k] = make_float4(duv[0], duv[1], duv[2], duv[3]);
+    } else {
+      *(float2*)&s_dt[row * TP + 2 * k] = make_float2(dtv[0], dtv[1]);
+      *(float2*)&s_du[row * TP + 2 * k] = make_float2(duv[0], duv[1]);
+    }
     wave_lds_sync();
 
     // The recurrence over the 32 steps for this lane's NS states.  Software
@@ -773,7 +790,7 @@ rowgroup_kernel(KParams p) {
     // group g computes, and a group's decay factors (independent of the state) are
     // all formed before its recurrence, so LDS and transcendental latencies overlap
     // with arithmetic instead of stalling the wave.
-    constexpr int NBC = (MODE == 0 ? 2 : 1) * NS;            // B (and C) floats per step
+    constexpr int NBC = 2 * NS;                               // B and C of the lane's states, interleaved
     float part[MODE == 0 ? TB : 1];
     float4 cur_dt, cur_du, nxt_dt, nxt_du;
     float cur_bc[4][NBC], nxt_bc[4][NBC];
@@ -782,11 +799,16 @@ rowgroup_kernel(KParams p) {
       du4 = *(const float4*)&s_du[row * TP + t4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float* src = &s_b[(t4 + q) * 2 * NPAD + k * 2 * NS];
+        const float* src = &s_b[((t4 + q) * NPAD + k * NS) * 2];
+        if constexpr (NBC == 2) {
+          const float2 v = *(const float2*)src;
+          bcv[q][0] = v.x; bcv[q][1] = v.y;
+        } else {
 #pragma unroll
-        for (int j = 0; j < NBC; j += 2) {
-          const float2 v = *(const float2*)&src[j];
-          bcv[q][j] = v.x; bcv[q][j + 1] = v.y;
+          for (int j = 0; j < NBC; j += 4) {
+            const float4 v = *(const float4*)&src[j];
+            bcv[q][j] = v.x; bcv[q][j + 1] = v.y; bcv[q][j + 2] = v.z; bcv[q][j + 3] = v.w;
+          }
         }
       }
     };
@@ -802,9 +824,9 @@ rowgroup_kernel(KParams p) {
         for (int j = 0; j < NS; ++j) {
           const float y = dtq[q] * A2[j];
           ca[q][j] = __builtin_amdgcn_exp2f(y);
-          cbx[q][j] = duq[q] * bcv[q][j];
+          cbx[q][j] = duq[q] * bcv[q][2 * j];
           if (kZOH) cbx[q][j] *= zoh_factor(y, ca[q][j]);
-          if (MODE == 0) cC[q][j] = bcv[q][NS + j];
+          if (MODE == 0) cC[q][j] = bcv[q][2 * j + 1];
         }
       }
     };
@@ -850,31 +872,39 @@ rowgroup_kernel(KParams p) {
         *(float4*)&s_part[(row * LPR + k) * TP + t4] =
             make_float4(part[t4], part[t4 + 1], part[t4 + 2], part[t4 + 3]);
       wave_lds_sync();
-      // sum of the 8 lanes' partials of this lane's 4 steps, as a pairwise tree
-      float4 pv[LPR];
+      // sum of the channel's LPR partials of this lane's steps, as a pairwise tree
+      float pv[LPR][QPL];
 #pragma unroll
-      for (int kk = 0; kk < LPR; ++kk) pv[kk] = *(const float4*)&s_part[(row * LPR + kk) * TP + 4 * k];
+      for (int kk = 0; kk < LPR; ++kk) {
+        const float* src = &s_part[(row * LPR + kk) * TP + QPL * k];
+        if constexpr (QPL == 4) {
+          const float4 v = *(const float4*)src;
+          pv[kk][0] = v.x; pv[kk][1] = v.y; pv[kk][2] = v.z; pv[kk][3] = v.w;
+        } else {
+          const float2 v = *(const float2*)src;
+          pv[kk][0] = v.x; pv[kk][1] = v.y;
+        }
+      }
 #pragma unroll
       for (int w = LPR / 2; w >= 1; w /= 2)
 #pragma unroll
-        for (int kk = 0; kk < w; ++kk) {
-          pv[kk].x += pv[kk + w].x; pv[kk].y += pv[kk + w].y;
-          pv[kk].z += pv[kk + w].z; pv[kk].w += pv[kk + w].w;
-        }
-      float ys[4] = {pv[0].x, pv[0].y, pv[0].z, pv[0].w};
+        for (int kk = 0; kk < w; ++kk)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float yv = fmaf(Dd, uu[q], ys[q]);
+          for (int q = 0; q < QPL; ++q) pv[kk][q] += pv[kk + w][q];
+      float ys[QPL];
+#pragma unroll
+      for (int q = 0; q < QPL; ++q) {
+        float yv = fmaf(Dd, uu[q], pv[0][q]);
         if (p.has_z) yv *= silu_f(zz[q]);
         ys[q] = yv;
       }
       char* const yb = py + tb * kB;
       if (VECOK && nvalid == TB) {
-        IO::stv4_stream(yb + loff, ys);
+        IO::template stv_stream<QPL>(yb + loff, ys);
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (4 * k + q < nvalid) IO::st(yb + loff, q, ys[q]);
+        for (int q = 0; q < QPL; ++q)
+          if (QPL * k + q < nvalid) IO::st(yb + loff, q, ys[q]);
       }
     }
     wave_lds_sync();     // the next block rewrites the tiles this one read
@@ -884,13 +914,13 @@ rowgroup_kernel(KParams p) {
   int64_t t_blk = t_seg0;
   if (VECOK) {
     const int64_t n_full = (t_seg1 - t_seg0) / TB;
-    Raw4 pf_dt, pf_u, pf_z;
+    RawQ pf_dt, pf_u, pf_z;
     f32x4 pf_bc[NQ];
     auto issue = [&](int64_t tb) {
       const int64_t ob = tb * kB;
-      pf_dt = *(const Raw4*)(pdl + ob + loff);
-      pf_u = *(const Raw4*)(pu + ob + loff);
-      if (MODE == 0) pf_z = *(const Raw4*)(pz + ob + loff);
+      pf_dt = *(const RawQ*)(pdl + ob + loff);
+      pf_u = *(const RawQ*)(pu + ob + loff);
+      if (MODE == 0) pf_z = *(const RawQ*)(pz + ob + loff);
       const f32x4* tl = tiles + (tb / TB) * (TILE_BC / 4);
 #pragma unroll
       for (int i = 0; i < NQ; ++i) pf_bc[i] = tl[lane + 64 * i];
@@ -899,10 +929,10 @@ rowgroup_kernel(KParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): only prefetches are in flight inside the loop
     for (int64_t it = 0; it < n_full; ++it, t_blk += TB) {
       // take the prefetched block out of the prefetch registers, then refill them
-      float raw[4], uu[4], zz[4];
-      IO::template unpack<4>(pf_dt, raw);
-      IO::template unpack<4>(pf_u, uu);
-      IO::template unpack<4>(pf_z, zz);
+      float raw[QPL], uu[QPL], zz[QPL];
+      IO::template unpack<QPL>(pf_dt, raw);
+      IO::template unpack<QPL>(pf_u, uu);
+      IO::template unpack<QPL>(pf_z, zz);
 #pragma unroll
       for (int i = 0; i < NQ; ++i) ((f32x4*)s_b)[lane + 64 * i] = pf_bc[i];
       issue(it + 1 < n_full ? t_blk + TB : t_blk);   // the last one re-reads this block (unused)
@@ -913,10 +943,10 @@ rowgroup_kernel(KParams p) {
   for (; t_blk < t_seg1; t_blk += TB) {
     const int nvalid = (int)min((int64_t)TB, t_seg1 - t_blk);
     const int64_t ob = t_blk * kB;
-    float raw[4], uu[4], zz[4];
+    float raw[QPL], uu[QPL], zz[QPL];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t i = 4 * k + q < nvalid ? q : -4 * k;     // clamped to step t_blk of the row
+    for (int q = 0; q < QPL; ++q) {
+      const int64_t i = QPL * k + q < nvalid ? q : -QPL * k;   // clamped to step t_blk of the row
       raw[q] = IO::cvt(IO::ld_bits(pdl + ob + loff, i));
       uu[q] = IO::cvt(IO::ld_bits(pu + ob + loff, i));
       zz[q] = (MODE == 0) ? IO::cvt(IO::ld_bits(pz + ob + loff, i)) : 0.0f;
@@ -958,6 +988,41 @@ rowgroup_kernel(KParams p) {
   }
 }
 
+// plain launch: 4 independent waves of 8 lanes per channel
+template <typename IO, int NS, int MODE, bool VECOK, bool CONV>
+__global__ void __launch_bounds__(rg::WPG * 64) __attribute__((amdgpu_waves_per_eu((CONV || IO::kBytes == 4) ? 3 : 1)))
+rowgroup_kernel(KParams p) {
+  using namespace rg;
+  __shared__ __attribute__((aligned(16))) float s_tile[WPG][TILE];
+  __shared__ __attribute__((aligned(16))) float s_bc[WPG][bc_tile<8 * NS>()];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = blockIdx.x * WPG + wv;
+  if (rb >= p.blocks_per_group * p.G) return;               // no barriers: idle waves may leave
+  rowgroup_wave<IO, 8, NS, MODE, VECOK, CONV>(p, rb / p.blocks_per_group, (rb % p.blocks_per_group) * 8,
+                                              s_tile[wv], s_bc[wv]);
+}
+
+// mixed launch (16 states): waves 0..7 take 8 channels each with 8 lanes per channel,
+// waves 8..11 take 4 channels each with 16 lanes per channel; 80 channels per workgroup
+template <typename IO, int MODE, bool VECOK>
+__global__ void __launch_bounds__(rg::MIX_WAVES * 64) rowgroup_mixed_kernel(KParams p) {
+  using namespace rg;
+  __shared__ __attribute__((aligned(16))) float s_tile[MIX_WAVES][TILE];
+  __shared__ __attribute__((aligned(16))) float s_bc[MIX_WAVES][bc_tile<16>()];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = blockIdx.x / p.blocks_per_group;
+  const int rbase = (blockIdx.x % p.blocks_per_group) * MIX_ROWS;
+  if (wv < 8) {
+    const int r0 = rbase + 8 * wv;
+    if (r0 >= p.rows_per_group) return;                      // no barriers: idle waves may leave
+    rowgroup_wave<IO, 8, 2, MODE, VECOK, false>(p, g, r0, s_tile[wv], s_bc[wv]);
+  } else {
+    const int r0 = rbase + 64 + 4 * (wv - 8);
+    if (r0 >= p.rows_per_group) return;
+    rowgroup_wave<IO, 16, 1, MODE, VECOK, false>(p, g, r0, s_tile[wv], s_bc[wv]);
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 template <int LAYOUT, typename IO, int NS, int NW, int TB, bool VECOK>
 int launch_modes(const Plan& pl, const KParams& kp, hipStream_t st) {
@@ -985,7 +1050,7 @@ int launch_rowgroup_modes(const Plan& pl, const KParams& kp, hipStream_t st) {
   const dim3 block(rg::WPG * 64);
   const int total = kp.blocks_per_group * kp.G;
   const int gx = (total + rg::WPG - 1) / rg::WPG;
-  hipLaunchKernelGGL((bc_tile_kernel<IO, NS>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
+  hipLaunchKernelGGL((bc_tile_kernel<IO, 8 * NS>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
   {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
@@ -1010,8 +1075,22 @@ int launch_rowgroup(const Plan& pl, const KParams& kp, hipStream_t st) {
   return launch_rowgroup_modes<IO, NS, false, false>(pl, kp, st);
 }
 
+template <typename IO, bool VECOK>
+int launch_rowgroup_mixed(const KParams& kp, hipStream_t st) {
+  hipLaunchKernelGGL((bc_tile_kernel<IO, 16>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL((rowgroup_mixed_kernel<IO, 0, VECOK>), dim3(kp.blocks_per_group * kp.G, kp.batch, 1),
+                     dim3(rg::MIX_WAVES * 64), 0, st, kp);
+  return (int)hipGetLastError();
+}
+
 template <int LAYOUT, typename IO>
 int launch_io(const Plan& pl, const KParams& kp, hipStream_t st) {
+  if (LAYOUT == 0 && pl.kernel == 3) {
+    if (kp.L % 4 == 0) return launch_rowgroup_mixed<IO, true>(kp, st);
+    return launch_rowgroup_mixed<IO, false>(kp, st);
+  }
   if (LAYOUT == 0 && pl.kernel == 1) {
     if (pl.Npad == 16) return launch_rowgroup<IO, 2>(pl, kp, st);
     if (pl.Npad == 32) return launch_rowgroup<IO, 4>(pl, kp, st);

@@ -17,7 +17,8 @@ namespace ssm {
 
 struct Plan {
   int kernel = 0;            // 0: workgroup kernel (64 rows, states over waves); 1: row-group kernel;
-                             // 2: chunked multi-head kernel on MFMA (ssd_kernels.hip)
+                             // 2: chunked multi-head kernel on MFMA (ssd_kernels.hip);
+                             // 3: row-group kernel, mixed launch (16 states, 80 channels per workgroup)
   int ps = 0;                // kernel 2: positions per workgroup
   int disc = 0;              // SSM_DISC_DELTA_B or SSM_DISC_ZOH
   int layout = 0, io = 0;
@@ -58,7 +59,7 @@ struct KParams {
   int64_t L, seg_len;
   int batch, dim, N, Npad, H, P, G;
   int rows_per_group;    // BDL: dim / G;  BLHP: P
-  int blocks_per_group;  // row blocks per group / head (64 rows, or 8 for the row-group kernel)
+  int blocks_per_group;  // row blocks per group / head (64 rows; 8 for the row-group kernel, 80 mixed)
   int heads_per_group;   // BLHP: H / G
   int softplus;
   int has_z;
@@ -88,7 +89,8 @@ struct UParams {
 };
 
 // Validates dims (no HIP call) and fills the plan; returns SSM_OK or an error code.
-int make_plan(const ssm_dims_t* d, Plan* plan);
+// allow_mixed = false keeps the plain row-group launch (the fused input stage needs it).
+int make_plan(const ssm_dims_t* d, Plan* plan, bool allow_mixed = true);
 
 // Enqueue the kernels of a validated plan.  Returns a hipError_t value (0 = success).
 // scan_kernels.hip is compiled once per discretization; launch_plan picks the build.

@@ -199,3 +199,46 @@ def test_continuation_matches_single_call():
     y2, h2 = gpu_run(second)
     torch.testing.assert_close(torch.cat([y1, y2], dim=2), y, rtol=2e-5, atol=2e-5)
     torch.testing.assert_close(h2, h, rtol=2e-5, atol=2e-5)
+
+
+# ------------------------------------------------------------------ launch shapes for 16 states
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("D,L,G", [(1, 33, 1), (7, 100, 1), (80, 64, 1), (100, 77, 1), (161, 256, 1),
+                                   (240, 1, 1), (200, 130, 2), (160, 96, 2)])
+def test_mixed_launch(io, D, L, G, monkeypatch):
+    """Workgroups of 8-lane and 16-lane channel waves (80 channels each) against the oracle,
+    including partial workgroups, channel counts not a multiple of 4 or 8, and groups."""
+    monkeypatch.setenv("SSM_SCAN_MIXED", "1")
+    c = make_case("mixed", layout="bdl", io_dtype=io, batch=2, seqlen=L, dim=D, dstate=16, ngroups=G,
+                  seed=D * 7 + L, has_h0=True, A_kind="lognormal")
+    assert "kernel=rowgroup_mixed" in scan.describe(scan.make_dims("bdl", io, 2, L, D, 16, ngroups=G))
+    check_case(c)
+
+
+@pytest.mark.parametrize("opts", [dict(has_z=False), dict(has_D=False, has_bias=False), dict(delta_kind="wide")])
+def test_mixed_launch_options(opts, monkeypatch):
+    monkeypatch.setenv("SSM_SCAN_MIXED", "1")
+    c = make_case("mixed_opts", layout="bdl", io_dtype="bf16", batch=3, seqlen=200, dim=170, dstate=13, seed=9,
+                  has_h0=True, A_kind="lognormal", **opts)
+    check_case(c)
+
+
+def test_mixed_and_plain_agree():
+    """Both launches of the 16-state layer: the same recurrence per state; only the order of the
+    readout sum over states differs."""
+    c = make_case("mix_vs_plain", layout="bdl", io_dtype="bf16", batch=2, seqlen=512, dim=320, dstate=16,
+                  seed=12, has_h0=True, A_kind="lognormal")
+    old = os.environ.get("SSM_SCAN_MIXED")
+    try:
+        os.environ["SSM_SCAN_MIXED"] = "1"
+        y1, h1 = gpu_run(c)
+        os.environ["SSM_SCAN_MIXED"] = "0"
+        y0, h0 = gpu_run(c)
+    finally:
+        if old is None:
+            os.environ.pop("SSM_SCAN_MIXED", None)
+        else:
+            os.environ["SSM_SCAN_MIXED"] = old
+    torch.testing.assert_close(y1.float(), y0.float(), rtol=1e-2, atol=1e-2)
+    torch.testing.assert_close(h1, h0, rtol=1e-5, atol=1e-5)
