@@ -147,10 +147,14 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
     p.bc_bytes = (size_t)d->batch * (size_t)d->ngroups * (size_t)p.nblk * (size_t)p.TB * 2 * (size_t)p.Npad *
                  sizeof(float);
     p.bc_bytes = (p.bc_bytes + 255) & ~(size_t)255;
-    // 16 states in one segment: the mixed launch (80 channels per workgroup, one
-    // workgroup per CU, the same work on every SIMD) when its busiest SIMD has less
-    // to do than the plain launch's.  A workgroup costs about 2.6 plain waves of
-    // work per SIMD.  SSM_SCAN_MIXED=0/1 forces the choice (tests, tuning).
+    // 16 states in one segment: an 80-channel launch (one workgroup per CU, the same
+    // work on every SIMD) when its busiest SIMD has less to do than the plain launch's.
+    // A workgroup costs about 2.6 plain waves of work per SIMD.  SSM_SCAN_MIXED=0/1
+    // forces the choice (tests, tuning).  The 80-channel launch is the mixed one (8 and
+    // 16 lanes per channel, independent waves); SSM_SCAN_SPLIT=4 or 2 selects the split
+    // one instead (states over waves, 4 or 2 per wave, B/C in scalar registers, two
+    // workgroup barriers per block; its tiles take twice the workspace), which measured
+    // slower on MI355X: its waves stall at the barriers.
     if (allow_mixed && p.Npad == 16 && p.nseg == 1) {
       const int64_t mixed_blocks = (rows_per_group + 79) / 80;
       const int64_t wgs = mixed_blocks * groups_or_heads * d->batch;
@@ -161,9 +165,14 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
       const char* env = std::getenv("SSM_SCAN_MIXED");
       if (env && *env) mixed = *env != '0';
       if (mixed && groups_or_heads * mixed_blocks <= 0x7fffffff) {
-        p.kernel = 3;
+        const char* senv = std::getenv("SSM_SCAN_SPLIT");
+        const bool split = senv && (*senv == '2' || *senv == '4');
+        p.kernel = split ? 4 : 3;
+        p.ps = split ? *senv - '0' : 0;   // split launch: states per state wave
+        if (p.kernel == 4 && p.ps == 4) p.vec_ok = p.vec_ok && d->seqlen % 8 == 0;   // 8-step vectors
         p.blocks_per_group = (int)mixed_blocks;
         p.grid_rows = (int)(groups_or_heads * mixed_blocks);
+        if (p.kernel == 4) p.bc_bytes *= 2;
       }
     }
   }
@@ -210,12 +219,16 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
   if (buf && buf_len) {
     std::snprintf(buf, buf_len,
                   "kernel=%s layout=%s io=%s disc=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d "
-                  "ws=%zu",
-                  p.kernel == 3 ? "rowgroup_mixed" : p.kernel == 2 ? "ssd" : p.kernel == 1 ? "rowgroup" : "workgroup",
+                  "ws=%zu%s",
+                  p.kernel == 4   ? "rowgroup_split"
+                  : p.kernel == 3 ? "rowgroup_mixed"
+                  : p.kernel == 2 ? "ssd"
+                  : p.kernel == 1 ? "rowgroup"
+                                  : "workgroup",
                   p.layout == SSM_LAYOUT_BDL ? "bdl" : "blhp",
                   p.io == SSM_BF16 ? "bf16" : "f32", p.disc == SSM_DISC_ZOH ? "zoh" : "delta_b", p.NS, p.NW, p.TB,
                   p.Npad, p.grid_rows, (long long)dims->batch, p.nseg, (long long)p.seg_len, (int)p.vec_ok,
-                  p.ws_bytes);
+                  p.ws_bytes, p.kernel == 4 ? (p.ps == 2 ? " states_per_wave=2" : " states_per_wave=4") : "");
   }
   return SSM_OK;
 }
@@ -301,6 +314,7 @@ static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, 
   kp.h0 = h0; kp.y = y; kp.h_last = h_last;
   const size_t half = pl.seg_bytes / 2 / sizeof(float);
   kp.bct = pl.bc_bytes ? (float*)ws : nullptr;
+  kp.bct2 = pl.kernel == 4 ? (float*)((char*)ws + pl.bc_bytes / 2) : nullptr;   // second half of the tiles
   kp.nblk = pl.nblk;
   kp.wsP = pl.seg_bytes ? (float*)((char*)ws + pl.bc_bytes) : nullptr;
   kp.wsH = pl.seg_bytes ? kp.wsP + half : nullptr;

@@ -18,7 +18,8 @@ namespace ssm {
 struct Plan {
   int kernel = 0;            // 0: workgroup kernel (64 rows, states over waves); 1: row-group kernel;
                              // 2: chunked multi-head kernel on MFMA (ssd_kernels.hip);
-                             // 3: row-group kernel, mixed launch (16 states, 80 channels per workgroup)
+                             // 3: row-group kernel, mixed launch (16 states, 80 channels per workgroup);
+                             // 4: row-group kernel, split launch (16 states, 80 channels per workgroup)
   int ps = 0;                // kernel 2: positions per workgroup
   int disc = 0;              // SSM_DISC_DELTA_B or SSM_DISC_ZOH
   int layout = 0, io = 0;
@@ -50,6 +51,7 @@ struct KParams {
   float* wsP;   // [seg][b][n][d] decay product of each aggregated segment
   float* wsH;   // [seg][b][n][d] zero-start end state of each aggregated segment
   float* bct;   // row-group kernel: [b][g][block] B/C tiles in LDS order (bc_tile_kernel)
+  float* bct2;  // split launch: the same tiles per state pair, [b][g][block][pair][t][B C B C]
   const float* conv_w;     // optional input stage (row-group kernel): (dim, conv_k) filters
   const float* conv_b;     // (dim) or NULL
   const float* conv_sin;   // (batch, dim, conv_k-1) raw inputs before t = 0, or NULL (zeros)

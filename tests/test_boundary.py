@@ -129,7 +129,7 @@ def test_workspace_size_and_plan():
     assert scan.workspace_size(d) == bc_tile_bytes(4, 2048, 16)
     assert "seg_len=2048" in scan.describe(d)
     txt = scan.describe(d)
-    assert "kernel=rowgroup_mixed" in txt and "layout=bdl" in txt and "NS=2" in txt and "grid=(64,4,1)" in txt
+    assert "kernel=rowgroup_mixed" in txt and "layout=bdl" in txt and "grid=(64,4,1)" in txt
     d2 = dims(batch=8, seqlen=2048, dim=1536, dstate=16)              # 1536 waves: the plain launch
     assert "kernel=rowgroup " in scan.describe(d2) and "grid=(48,8,1)" in scan.describe(d2)
     d32 = dims(batch=4, seqlen=2048, dim=5120, dstate=32)             # 32 states: plain
@@ -153,7 +153,7 @@ def test_segment_override_env(monkeypatch):
     monkeypatch.setenv("SSM_SCAN_SEGMENTS", "4")
     assert scan.workspace_size(d) == bc_tile_bytes(4, 2048, 16) + 2 * 3 * 4 * 16 * 5120 * 4
     monkeypatch.setenv("SSM_SCAN_SEGMENTS", "1")
-    assert scan.workspace_size(d) == bc_tile_bytes(4, 2048, 16)
+    assert scan.workspace_size(d) == bc_tile_bytes(4, 2048, 16)       # one segment: the mixed launch
     d = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
     assert scan.workspace_size(d) == 0                                 # workgroup kernel, one segment
 
@@ -234,7 +234,7 @@ def test_ssd_override_env(monkeypatch):
 
 
 def test_mixed_launch_override_env(monkeypatch):
-    """SSM_SCAN_MIXED forces the 16-state launch shape; the workspace does not depend on it."""
+    """SSM_SCAN_MIXED forces the 16-state launch shape, SSM_SCAN_SPLIT=4/2 the split 80-channel one."""
     d = dims(batch=4, seqlen=2048, dim=5120, dstate=16)
     ws = scan.workspace_size(d)
     monkeypatch.setenv("SSM_SCAN_MIXED", "0")
@@ -242,5 +242,10 @@ def test_mixed_launch_override_env(monkeypatch):
     monkeypatch.setenv("SSM_SCAN_MIXED", "1")
     d2 = dims(batch=8, seqlen=2048, dim=1536, dstate=16)
     assert "kernel=rowgroup_mixed" in scan.describe(d2) and "grid=(20,8,1)" in scan.describe(d2)
+    monkeypatch.setenv("SSM_SCAN_SPLIT", "2")
+    assert "kernel=rowgroup_split" in scan.describe(d2) and "states_per_wave=2" in scan.describe(d2)
+    monkeypatch.setenv("SSM_SCAN_SPLIT", "4")
+    assert "kernel=rowgroup_split" in scan.describe(d2) and "states_per_wave=4" in scan.describe(d2)
+    assert scan.workspace_size(d) == 2 * ws                             # two tile layouts
     d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # segmented: never mixed
     assert "kernel=rowgroup " in scan.describe(d4)

@@ -203,42 +203,63 @@ def test_continuation_matches_single_call():
 
 # ------------------------------------------------------------------ launch shapes for 16 states
 
+LAUNCH16 = {"split4": ("4", "kernel=rowgroup_split", "states_per_wave=4"),
+            "split2": ("2", "kernel=rowgroup_split", "states_per_wave=2"),
+            "mixed": ("0", "kernel=rowgroup_mixed", "")}
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("D,L,G", [(1, 33, 1), (7, 100, 1), (80, 64, 1), (100, 77, 1), (161, 256, 1),
-                                   (240, 1, 1), (200, 130, 2), (160, 96, 2)])
-def test_mixed_launch(io, D, L, G, monkeypatch):
-    """Workgroups of 8-lane and 16-lane channel waves (80 channels each) against the oracle,
-    including partial workgroups, channel counts not a multiple of 4 or 8, and groups."""
+                                   (240, 1, 1), (200, 130, 2), (160, 96, 2), (90, 36, 1), (64, 2052, 1)])
+@pytest.mark.parametrize("launch", list(LAUNCH16))
+def test_mixed_launch(io, D, L, G, launch, monkeypatch):
+    """The 80-channel launches against the oracle: split (states over waves, one channel per
+    lane, 4 or 2 states per wave, plus 16-lane waves) and mixed (8-lane and 16-lane channel
+    waves); partial workgroups, channel counts not a multiple of 4 or 8, one step, lengths
+    not a multiple of 4 or 8, groups."""
+    env, kname, extra = LAUNCH16[launch]
     monkeypatch.setenv("SSM_SCAN_MIXED", "1")
+    monkeypatch.setenv("SSM_SCAN_SPLIT", env)
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", "1")   # the 80-channel launches run one time segment
     c = make_case("mixed", layout="bdl", io_dtype=io, batch=2, seqlen=L, dim=D, dstate=16, ngroups=G,
                   seed=D * 7 + L, has_h0=True, A_kind="lognormal")
-    assert "kernel=rowgroup_mixed" in scan.describe(scan.make_dims("bdl", io, 2, L, D, 16, ngroups=G))
+    txt = scan.describe(scan.make_dims("bdl", io, 2, L, D, 16, ngroups=G))
+    assert kname in txt and extra in txt
     check_case(c)
 
 
+@pytest.mark.parametrize("launch", list(LAUNCH16))
 @pytest.mark.parametrize("opts", [dict(has_z=False), dict(has_D=False, has_bias=False), dict(delta_kind="wide")])
-def test_mixed_launch_options(opts, monkeypatch):
+def test_mixed_launch_options(opts, launch, monkeypatch):
     monkeypatch.setenv("SSM_SCAN_MIXED", "1")
+    monkeypatch.setenv("SSM_SCAN_SPLIT", LAUNCH16[launch][0])
     c = make_case("mixed_opts", layout="bdl", io_dtype="bf16", batch=3, seqlen=200, dim=170, dstate=13, seed=9,
                   has_h0=True, A_kind="lognormal", **opts)
     check_case(c)
 
 
 def test_mixed_and_plain_agree():
-    """Both launches of the 16-state layer: the same recurrence per state; only the order of the
-    readout sum over states differs."""
+    """The three launches of the 16-state layer: the same recurrence per state; only the order
+    of the readout sum over states differs."""
     c = make_case("mix_vs_plain", layout="bdl", io_dtype="bf16", batch=2, seqlen=512, dim=320, dstate=16,
                   seed=12, has_h0=True, A_kind="lognormal")
-    old = os.environ.get("SSM_SCAN_MIXED")
+    saved = {k: os.environ.get(k) for k in ("SSM_SCAN_MIXED", "SSM_SCAN_SPLIT")}
     try:
         os.environ["SSM_SCAN_MIXED"] = "1"
+        os.environ["SSM_SCAN_SPLIT"] = "4"
+        y3, h3 = gpu_run(c)
+        os.environ["SSM_SCAN_SPLIT"] = "2"
+        y2, h2 = gpu_run(c)
+        os.environ["SSM_SCAN_SPLIT"] = "0"
         y1, h1 = gpu_run(c)
         os.environ["SSM_SCAN_MIXED"] = "0"
         y0, h0 = gpu_run(c)
     finally:
-        if old is None:
-            os.environ.pop("SSM_SCAN_MIXED", None)
-        else:
-            os.environ["SSM_SCAN_MIXED"] = old
-    torch.testing.assert_close(y1.float(), y0.float(), rtol=1e-2, atol=1e-2)
-    torch.testing.assert_close(h1, h0, rtol=1e-5, atol=1e-5)
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    for y, h in ((y1, h1), (y2, h2), (y3, h3)):
+        torch.testing.assert_close(y.float(), y0.float(), rtol=1e-2, atol=1e-2)
+        torch.testing.assert_close(h, h0, rtol=1e-5, atol=1e-5)
