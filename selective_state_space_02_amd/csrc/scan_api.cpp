@@ -150,11 +150,13 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
     // 16 states in one segment: an 80-channel launch (one workgroup per CU, the same
     // work on every SIMD) when its busiest SIMD has less to do than the plain launch's.
     // A workgroup costs about 2.6 plain waves of work per SIMD.  SSM_SCAN_MIXED=0/1
-    // forces the choice (tests, tuning).  The 80-channel launch is the mixed one (8 and
-    // 16 lanes per channel, independent waves); SSM_SCAN_SPLIT=4 or 2 selects the split
-    // one instead (states over waves, 4 or 2 per wave, B/C in scalar registers, two
-    // workgroup barriers per block; its tiles take twice the workspace), which measured
-    // slower on MI355X: its waves stall at the barriers.
+    // forces the choice (tests, tuning).  The 80-channel launch is the mixed one with 4
+    // and 16 lanes per channel (independent waves, two per SIMD); SSM_SCAN_MIXED4=0 gives
+    // 8 and 16 lanes per channel (three waves per SIMD), SSM_SCAN_SPLIT=4 or 2 the split
+    // one (states over waves, 4 or 2 per wave, B/C in scalar registers, two workgroup
+    // barriers per block; its tiles take twice the workspace).  Both measured slower on
+    // MI355X: the first spends more instructions and LDS traffic per element, the second
+    // stalls at its barriers.
     if (allow_mixed && p.Npad == 16 && p.nseg == 1) {
       const int64_t mixed_blocks = (rows_per_group + 79) / 80;
       const int64_t wgs = mixed_blocks * groups_or_heads * d->batch;
@@ -167,8 +169,11 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
       if (mixed && groups_or_heads * mixed_blocks <= 0x7fffffff) {
         const char* senv = std::getenv("SSM_SCAN_SPLIT");
         const bool split = senv && (*senv == '2' || *senv == '4');
-        p.kernel = split ? 4 : 3;
+        const char* m4env = std::getenv("SSM_SCAN_MIXED4");
+        const bool mixed4 = !(m4env && *m4env == '0');
+        p.kernel = split ? 4 : mixed4 ? 5 : 3;
         p.ps = split ? *senv - '0' : 0;   // split launch: states per state wave
+        if (p.kernel == 5) p.vec_ok = p.vec_ok && d->seqlen % 8 == 0;   // 8-step vectors
         if (p.kernel == 4 && p.ps == 4) p.vec_ok = p.vec_ok && d->seqlen % 8 == 0;   // 8-step vectors
         p.blocks_per_group = (int)mixed_blocks;
         p.grid_rows = (int)(groups_or_heads * mixed_blocks);
@@ -220,7 +225,8 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
     std::snprintf(buf, buf_len,
                   "kernel=%s layout=%s io=%s disc=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d "
                   "ws=%zu%s",
-                  p.kernel == 4   ? "rowgroup_split"
+                  p.kernel == 5   ? "rowgroup_mixed4"
+                  : p.kernel == 4 ? "rowgroup_split"
                   : p.kernel == 3 ? "rowgroup_mixed"
                   : p.kernel == 2 ? "ssd"
                   : p.kernel == 1 ? "rowgroup"

@@ -164,14 +164,14 @@ struct BF16IO {
 };
 
 // ------------------------------------------------------------ elementwise math
-// softplus(r) = log(1 + e^r) = max(r, 0) + log1p(e^-|r|).  log1p(e) is taken as
-// log(w) + (e - (w - 1)) with w = 1 + e rounded: the second term is the exact
-// rounding error of w, which keeps full relative accuracy when e is tiny.
+// softplus(r) = log(1 + e^r) = max(r, 0) + log1p(e^-|r|), with log1p(e) taken as
+// ln 2 * log2(1 + e).  1 + e lies in [1, 2], so nothing overflows; rounding 1 + e
+// leaves an absolute error of about 2^-24 in the step size, which is far below the
+// step sizes whose value matters (the step only enters the state through dt*u*B and
+// exp(dt*A), both of which vanish with dt).
 __device__ __forceinline__ float softplus_f(float r) {
   const float e = __builtin_amdgcn_exp2f(-fabsf(r) * kLog2e);
-  const float w = 1.0f + e;
-  const float err = e - (w - 1.0f);
-  return (r > 0.0f ? r : 0.0f) + fmaf(__builtin_amdgcn_logf(w), kLn2, err);
+  return fmaf(__builtin_amdgcn_logf(1.0f + e), kLn2, r > 0.0f ? r : 0.0f);
 }
 
 // SiLU(z) = z / (1 + e^-z)
@@ -663,7 +663,10 @@ __device__ __forceinline__ void wg_lds_barrier() {
 
 // The body of one wave: channels r0 .. r0+64/LPR-1 of group g (clamped at the group's end).
 // BAR: the wave takes part in two workgroup barriers per time block (split launch).
-template <typename IO, int LPR, int NS, int MODE, bool VECOK, bool CONV, bool BAR = false>
+// SPF / HZF: softplus on the step and the z gate fixed at compile time (0/1), or -1 to
+// read them from the parameters.
+template <typename IO, int LPR, int NS, int MODE, bool VECOK, bool CONV, bool BAR = false, int SPF = -1,
+          int HZF = -1>
 __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, float* s_tile, float* s_bc) {
   using namespace rg;
   constexpr int RPW = 64 / LPR;                              // channels per wave
@@ -672,12 +675,15 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
   constexpr int NPAD = LPR * NS;
   constexpr int TILE_BC = bc_tile<NPAD>();
   constexpr int NQ = TILE_BC / (64 * 4);                     // float4 of the B/C tile per lane
-  using RawQ = typename RawT<QPL * kB>::T;                   // QPL steps of one tensor
-  static_assert(QPL == 4 || QPL == 2, "8 or 16 lanes per channel");
+  constexpr int NCK = QPL * kB > 16 ? QPL * kB / 16 : 1;      // 16-byte chunks of QPL steps
+  using RawQ = typename RawT<QPL * kB / NCK>::T;             // one chunk of one tensor
+  static_assert(QPL == 8 || QPL == 4 || QPL == 2, "4, 8 or 16 lanes per channel");
   static_assert(!CONV || QPL == 4, "the input stage needs 4 steps per lane");
 
   const int lane = threadIdx.x & 63;
   const int row = lane / LPR, k = lane % LPR;
+  const bool use_sp = SPF < 0 ? p.softplus != 0 : SPF != 0;
+  const bool use_z = HZF < 0 ? p.has_z != 0 : HZF != 0;
   float* const s_dt = s_tile;
   float* const s_du = s_tile + RPW * TP;
   float* const s_part = s_tile;
@@ -785,13 +791,16 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
       const bool ok = QPL * k + q < nvalid;
       const float rr = raw[q] + bias;
       const float sp = softplus_f(rr);                        // branch-free: the steps interleave
-      const float dt = ok ? (p.softplus ? sp : rr) : 0.0f;
+      const float dt = ok ? (use_sp ? sp : rr) : 0.0f;
       dtv[q] = dt;
       duv[q] = dt * uu[q];
     }
-    if constexpr (QPL == 4) {
-      *(float4*)&s_dt[row * TP + 4 * k] = make_float4(dtv[0], dtv[1], dtv[2], dtv[3]);
-      *(float4*)&s_du[row * TP + 4 * k] = make_float4(duv[0], duv[1], duv[2], duv[3]);
+    if constexpr (QPL >= 4) {
+#pragma unroll
+      for (int q = 0; q < QPL; q += 4) {
+        *(float4*)&s_dt[row * TP + QPL * k + q] = make_float4(dtv[q], dtv[q + 1], dtv[q + 2], dtv[q + 3]);
+        *(float4*)&s_du[row * TP + QPL * k + q] = make_float4(duv[q], duv[q + 1], duv[q + 2], duv[q + 3]);
+      }
     } else {
       *(float2*)&s_dt[row * TP + 2 * k] = make_float2(dtv[0], dtv[1]);
       *(float2*)&s_du[row * TP + 2 * k] = make_float2(duv[0], duv[1]);
@@ -890,9 +899,12 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
 #pragma unroll
       for (int kk = 0; kk < LPR; ++kk) {
         const float* src = &s_part[(row * LPR + kk) * TP + QPL * k];
-        if constexpr (QPL == 4) {
-          const float4 v = *(const float4*)src;
-          pv[kk][0] = v.x; pv[kk][1] = v.y; pv[kk][2] = v.z; pv[kk][3] = v.w;
+        if constexpr (QPL >= 4) {
+#pragma unroll
+          for (int q = 0; q < QPL; q += 4) {
+            const float4 v = *(const float4*)(src + q);
+            pv[kk][q] = v.x; pv[kk][q + 1] = v.y; pv[kk][q + 2] = v.z; pv[kk][q + 3] = v.w;
+          }
         } else {
           const float2 v = *(const float2*)src;
           pv[kk][0] = v.x; pv[kk][1] = v.y;
@@ -908,12 +920,14 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
 #pragma unroll
       for (int q = 0; q < QPL; ++q) {
         float yv = fmaf(Dd, uu[q], pv[0][q]);
-        if (p.has_z) yv *= silu_f(zz[q]);
+        if (use_z) yv *= silu_f(zz[q]);
         ys[q] = yv;
       }
       char* const yb = py + tb * kB;
       if (VECOK && nvalid == TB) {
-        IO::template stv_stream<QPL>(yb + loff, ys);
+#pragma unroll
+        for (int q = 0; q < QPL; q += (QPL < 4 ? QPL : 4))
+          IO::template stv_stream<(QPL < 4 ? QPL : 4)>(yb + loff + q * kB, ys + q);
       } else {
 #pragma unroll
         for (int q = 0; q < QPL; ++q)
@@ -932,7 +946,7 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
       const int64_t i = QPL * k + q < nvalid ? q : -QPL * k;   // clamped to step tb of the row
       raw[q] = IO::cvt(IO::ld_bits(pdl + ob + loff, i));
       uu[q] = IO::cvt(IO::ld_bits(pu + ob + loff, i));
-      zz[q] = (MODE == 0) ? IO::cvt(IO::ld_bits(pz + ob + loff, i)) : 0.0f;
+      zz[q] = (MODE == 0 && HZF != 0) ? IO::cvt(IO::ld_bits(pz + ob + loff, i)) : 0.0f;
     }
     const f32x4* tl = tiles + (tb / TB) * (TILE_BC / 4);
 #pragma unroll
@@ -943,13 +957,16 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
   // ------------------------------------------------- full blocks, prefetched
   if (VECOK) {
     const int64_t n_full = (t_seg1 - t_blk) / TB;
-    RawQ pf_dt, pf_u, pf_z;
+    RawQ pf_dt[NCK], pf_u[NCK], pf_z[NCK];
     f32x4 pf_bc[NQ];
     auto issue = [&](int64_t tb) {
       const int64_t ob = tb * kB;
-      pf_dt = *(const RawQ*)(pdl + ob + loff);
-      pf_u = *(const RawQ*)(pu + ob + loff);
-      if (MODE == 0) pf_z = *(const RawQ*)(pz + ob + loff);
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) {
+        pf_dt[c] = ((const RawQ*)(pdl + ob + loff))[c];
+        pf_u[c] = ((const RawQ*)(pu + ob + loff))[c];
+        if (MODE == 0 && HZF != 0) pf_z[c] = ((const RawQ*)(pz + ob + loff))[c];
+      }
       const f32x4* tl = tiles + (tb / TB) * (TILE_BC / 4);
 #pragma unroll
       for (int i = 0; i < NQ; ++i) pf_bc[i] = tl[lane + 64 * i];
@@ -959,9 +976,12 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
     for (int64_t it = 0; it < n_full; ++it, t_blk += TB) {
       // take the prefetched block out of the prefetch registers, then refill them
       float raw[QPL], uu[QPL], zz[QPL];
-      IO::template unpack<QPL>(pf_dt, raw);
-      IO::template unpack<QPL>(pf_u, uu);
-      IO::template unpack<QPL>(pf_z, zz);
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) {
+        IO::template unpack<QPL / NCK>(pf_dt[c], raw + c * (QPL / NCK));
+        IO::template unpack<QPL / NCK>(pf_u[c], uu + c * (QPL / NCK));
+        IO::template unpack<QPL / NCK>(pf_z[c], zz + c * (QPL / NCK));
+      }
 #pragma unroll
       for (int i = 0; i < NQ; ++i) ((f32x4*)s_b)[lane + 64 * i] = pf_bc[i];
       issue(it + 1 < n_full ? t_blk + TB : t_blk);   // the last one re-reads this block (unused)
@@ -1034,6 +1054,29 @@ __global__ void __launch_bounds__(rg::MIX_WAVES * 64) rowgroup_mixed_kernel(KPar
     const int r0 = rbase + 64 + 4 * (wv - 8);
     if (r0 >= p.rows_per_group) return;
     rowgroup_wave<IO, 16, 1, MODE, VECOK, false>(p, g, r0, s_tile[wv], s_bc[wv]);
+  }
+}
+
+// mixed launch with 4 lanes per channel (16 states): waves 0..3 take 16 channels each with
+// 4 lanes of 4 states per channel, waves 4..7 take 4 channels each with 16 lanes per channel;
+// 80 channels per workgroup, waves w and w+4 share a SIMD.  Two waves per SIMD, but per
+// element a quarter less non-recurrence work and LDS traffic than 8 lanes per channel.
+template <typename IO, int MODE, bool VECOK, int SPF, int HZF>
+__global__ void __launch_bounds__(8 * 64) rowgroup_mixed4_kernel(KParams p) {
+  using namespace rg;
+  __shared__ __attribute__((aligned(16))) float s_tile[8][TILE];
+  __shared__ __attribute__((aligned(16))) float s_bc[8][bc_tile<16>()];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = blockIdx.x / p.blocks_per_group;
+  const int rbase = (blockIdx.x % p.blocks_per_group) * MIX_ROWS;
+  if (wv < 4) {
+    const int r0 = rbase + 16 * wv;
+    if (r0 >= p.rows_per_group) return;                      // no barriers: idle waves may leave
+    rowgroup_wave<IO, 4, 4, MODE, VECOK, false, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
+  } else {
+    const int r0 = rbase + 64 + 4 * (wv - 4);
+    if (r0 >= p.rows_per_group) return;
+    rowgroup_wave<IO, 16, 1, MODE, VECOK, false, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
   }
 }
 
@@ -1383,8 +1426,30 @@ int launch_rowgroup_split(const KParams& kp, hipStream_t st) {
   return (int)hipGetLastError();
 }
 
+template <typename IO, bool VECOK, int SPF, int HZF>
+int launch_rowgroup_mixed4_f(const KParams& kp, hipStream_t st) {
+  hipLaunchKernelGGL((bc_tile_kernel<IO, 16>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL((rowgroup_mixed4_kernel<IO, 0, VECOK, SPF, HZF>), dim3(kp.blocks_per_group * kp.G, kp.batch, 1),
+                     dim3(8 * 64), 0, st, kp);
+  return (int)hipGetLastError();
+}
+
+template <typename IO, bool VECOK>
+int launch_rowgroup_mixed4(const KParams& kp, hipStream_t st) {
+  if (kp.softplus) {
+    return kp.has_z ? launch_rowgroup_mixed4_f<IO, VECOK, 1, 1>(kp, st) : launch_rowgroup_mixed4_f<IO, VECOK, 1, 0>(kp, st);
+  }
+  return kp.has_z ? launch_rowgroup_mixed4_f<IO, VECOK, 0, 1>(kp, st) : launch_rowgroup_mixed4_f<IO, VECOK, 0, 0>(kp, st);
+}
+
 template <int LAYOUT, typename IO>
 int launch_io(const Plan& pl, const KParams& kp, hipStream_t st) {
+  if (LAYOUT == 0 && pl.kernel == 5) {
+    if (kp.L % 8 == 0) return launch_rowgroup_mixed4<IO, true>(kp, st);
+    return launch_rowgroup_mixed4<IO, false>(kp, st);
+  }
   if (LAYOUT == 0 && pl.kernel == 4) {
     if (pl.ps == 2) {
       if (kp.L % 4 == 0) return launch_rowgroup_split<IO, true, 2>(kp, st);

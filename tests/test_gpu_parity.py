@@ -203,9 +203,10 @@ def test_continuation_matches_single_call():
 
 # ------------------------------------------------------------------ launch shapes for 16 states
 
-LAUNCH16 = {"split4": ("4", "kernel=rowgroup_split", "states_per_wave=4"),
-            "split2": ("2", "kernel=rowgroup_split", "states_per_wave=2"),
-            "mixed": ("0", "kernel=rowgroup_mixed", "")}
+LAUNCH16 = {"split4": ({"SSM_SCAN_SPLIT": "4"}, "kernel=rowgroup_split", "states_per_wave=4"),
+            "split2": ({"SSM_SCAN_SPLIT": "2"}, "kernel=rowgroup_split", "states_per_wave=2"),
+            "mixed4": ({}, "kernel=rowgroup_mixed4", ""),
+            "mixed": ({"SSM_SCAN_MIXED4": "0"}, "kernel=rowgroup_mixed ", "")}
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -219,7 +220,8 @@ def test_mixed_launch(io, D, L, G, launch, monkeypatch):
     not a multiple of 4 or 8, groups."""
     env, kname, extra = LAUNCH16[launch]
     monkeypatch.setenv("SSM_SCAN_MIXED", "1")
-    monkeypatch.setenv("SSM_SCAN_SPLIT", env)
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
     monkeypatch.setenv("SSM_SCAN_SEGMENTS", "1")   # the 80-channel launches run one time segment
     c = make_case("mixed", layout="bdl", io_dtype=io, batch=2, seqlen=L, dim=D, dstate=16, ngroups=G,
                   seed=D * 7 + L, has_h0=True, A_kind="lognormal")
@@ -229,12 +231,17 @@ def test_mixed_launch(io, D, L, G, launch, monkeypatch):
 
 
 @pytest.mark.parametrize("launch", list(LAUNCH16))
-@pytest.mark.parametrize("opts", [dict(has_z=False), dict(has_D=False, has_bias=False), dict(delta_kind="wide")])
+@pytest.mark.parametrize("opts", [dict(has_z=False), dict(has_D=False, has_bias=False), dict(delta_kind="wide"),
+                                  dict(softplus=False, delta_kind="zero")])
 def test_mixed_launch_options(opts, launch, monkeypatch):
     monkeypatch.setenv("SSM_SCAN_MIXED", "1")
-    monkeypatch.setenv("SSM_SCAN_SPLIT", LAUNCH16[launch][0])
+    for k, v in LAUNCH16[launch][0].items():
+        monkeypatch.setenv(k, v)
+    opts = dict(opts)
+    softplus = opts.pop("softplus", True)
     c = make_case("mixed_opts", layout="bdl", io_dtype="bf16", batch=3, seqlen=200, dim=170, dstate=13, seed=9,
                   has_h0=True, A_kind="lognormal", **opts)
+    c.softplus = softplus
     check_case(c)
 
 
@@ -243,7 +250,7 @@ def test_mixed_and_plain_agree():
     of the readout sum over states differs."""
     c = make_case("mix_vs_plain", layout="bdl", io_dtype="bf16", batch=2, seqlen=512, dim=320, dstate=16,
                   seed=12, has_h0=True, A_kind="lognormal")
-    saved = {k: os.environ.get(k) for k in ("SSM_SCAN_MIXED", "SSM_SCAN_SPLIT")}
+    saved = {k: os.environ.get(k) for k in ("SSM_SCAN_MIXED", "SSM_SCAN_SPLIT", "SSM_SCAN_MIXED4")}
     try:
         os.environ["SSM_SCAN_MIXED"] = "1"
         os.environ["SSM_SCAN_SPLIT"] = "4"
@@ -251,7 +258,10 @@ def test_mixed_and_plain_agree():
         os.environ["SSM_SCAN_SPLIT"] = "2"
         y2, h2 = gpu_run(c)
         os.environ["SSM_SCAN_SPLIT"] = "0"
+        os.environ["SSM_SCAN_MIXED4"] = "0"
         y1, h1 = gpu_run(c)
+        os.environ["SSM_SCAN_MIXED4"] = "1"
+        y4, h4 = gpu_run(c)
         os.environ["SSM_SCAN_MIXED"] = "0"
         y0, h0 = gpu_run(c)
     finally:
@@ -260,6 +270,6 @@ def test_mixed_and_plain_agree():
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
-    for y, h in ((y1, h1), (y2, h2), (y3, h3)):
+    for y, h in ((y1, h1), (y2, h2), (y3, h3), (y4, h4)):
         torch.testing.assert_close(y.float(), y0.float(), rtol=1e-2, atol=1e-2)
         torch.testing.assert_close(h, h0, rtol=1e-5, atol=1e-5)
