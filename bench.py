@@ -70,12 +70,19 @@ def algorithmic_bytes(case) -> int:
     return total
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(workload: str) -> str:
+    """Hash of the sources the workload's kernels are built from (the host API plus the
+    kernel file of its path), so counters taken for one path stay valid while another changes."""
+    from selective_state_space_02_amd.inputs import DECODE_CONFIGS
+    if workload in DECODE_CONFIGS:
+        kern = "update_kernels.hip"
+    elif workload == "mamba2_multihead":
+        kern = "ssd_kernels.hip"
+    else:
+        kern = "scan_kernels.hip"
     h = hashlib.sha256()
-    for f in ("selective_state_space_02_amd/csrc/scan_kernels.hip", "selective_state_space_02_amd/csrc/scan_api.cpp",
-              "selective_state_space_02_amd/csrc/scan_plan.h", "selective_state_space_02_amd/csrc/update_kernels.hip",
-              "selective_state_space_02_amd/csrc/ssd_kernels.hip"):
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+    for f in ("scan_api.cpp", "scan_plan.h", kern):
+        h.update(open(os.path.join(ROOT, "selective_state_space_02_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -88,7 +95,7 @@ def load_traffic(workload: str):
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 
