@@ -124,9 +124,12 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
   const char* ssd_env = std::getenv("SSM_SCAN_SSD");
   const bool ssd_ok = !(ssd_env && *ssd_env == '0');
   if (ssd_ok && d->layout == SSM_LAYOUT_BLHP && d->io_dtype == SSM_BF16 && (N == 32 || N == 64 || N == 128) &&
-      d->headdim % 32 == 0 && d->nheads <= 65535) {
+      d->headdim % 16 == 0 && d->nheads <= 65535) {
     p.kernel = 2;
-    p.ps = d->headdim % 64 == 0 ? 64 : 32;
+    // positions per workgroup: 32 (two workgroups per CU), 16 when the head size needs it;
+    // SSM_SSD_PS=16 forces 16 (tests, tuning)
+    const char* ps_env = std::getenv("SSM_SSD_PS");
+    p.ps = (d->headdim % 32 == 0 && !(ps_env && std::atoi(ps_env) == 16)) ? 32 : 16;
     p.NS = 0; p.NW = 4; p.TB = 64;
     p.grid_rows = (int)(d->headdim / p.ps);
     p.nseg = 1;

@@ -10,15 +10,28 @@
 //         + D u_t, times SiLU(z_t)
 //   H'    = exp(cum_{Q-1}) H + sum_s exp(cum_{Q-1} - cum_s) B_s (x) X_s
 // which is the recurrence h_t = exp(dt_t A) h_{t-1} + dt_t B_t u_t, regrouped exactly.
-// The three contractions (C B^T over states, (L o C B^T) X over steps, C H over
-// states, B^T X over steps) run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
-// B and C are bfloat16 in memory, so they are exact operands.  The fp32 operands
-// that feed the output -- the decayed C B^T, dt*u and the state -- are split into a
-// bfloat16 high part and a bfloat16 remainder (x = hi + lo, |x - hi - lo| ~ 2^-17 |x|),
-// and the products take hi*hi + hi*lo + lo*hi (decay x input), C*hi + C*lo (state)
-// or B^T hi + B^T lo (chunk state), so the results keep about 16 bits instead of 8.
-// The state is carried in fp32.  One workgroup (4 waves) walks the chunks of one (batch, head,
-// slice of PS positions) in order with the state in registers.
+//
+// The contractions run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  B and C are
+// bfloat16 in memory, so they are exact operands.  The fp32 operands that feed the output
+// -- the decayed C B^T, dt*u, its decayed copy and the state -- are split into a bfloat16
+// high part and a bfloat16 remainder (x = hi + lo, |x - hi - lo| ~ 2^-17 |x|), and the
+// products take hi*hi + hi*lo + lo*hi (decay x input), C*hi + C*lo (state) or
+// B^T hi + B^T lo (chunk state), so the results keep about 16 bits instead of 8.  The
+// state is carried in fp32.
+//
+// Work split: one workgroup (4 waves) walks the chunks of one (batch item, head, slice of
+// PS positions) in order, with its slice of the state in registers; two workgroups fit on
+// a CU.  Everything is computed transposed (rows = positions or states, columns = steps),
+// so that each product's output tile is already in the layout its consumer reads:
+//   G^T = B C^T              -> M^T = G^T o decay, stored [t][s] with 8-byte writes
+//   Y^T = X^T M^T + H^T C^T  -> each lane holds 4 consecutive positions of one step: the
+//                               row of y is written with 8-byte stores
+//   H   = e^{cum_end} H + B^T (w X)  -> stored [p][n] with 8-byte writes for the next chunk
+// The operands whose contraction runs over steps (X^T, B^T, w X) are read from their
+// natural [step][.] layout with ds_read_b64_tr_b16, the gfx950 transposing LDS read: in
+// each group of 16 lanes, lane i receives element i % 4 of the 8-byte pieces addressed by
+// lanes 4k + i/4 (k = 0..3), so with lane j addressing row k0 + j/4, columns 4(j%4)..+3
+// of a [k][r] array, lane i gets column i of rows k0 .. k0+3.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,26 +43,30 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
-__device__ __forceinline__ uint16_t f2bf(float v) {
-  const bf16 b = (bf16)v;
-  return __builtin_bit_cast(uint16_t, b);
+__device__ __forceinline__ float bf2f(uint32_t v16) { return __uint_as_float(v16 << 16); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two floats to a packed bf16 pair (round to nearest even), one instruction
+__device__ __forceinline__ uint32_t pack_bf(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
-// x = bf16 hi + bf16 lo
-__device__ __forceinline__ void split_bf(float x, uint16_t& hi, uint16_t& lo) {
-  hi = f2bf(x);
-  lo = f2bf(x - bf2f(hi));
+// a = ah + al, b = bh + bl (bf16 parts); hi = ah | bh << 16, lo = al | bl << 16
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf(a, b);
+  lo = pack_bf(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
+// softplus(r) = max(r, 0) + ln 2 * log2(1 + 2^(-|r| log2 e)); 1 + e in [1, 2] never overflows
 __device__ __forceinline__ float softplus_s(float r) {
   const float e = __builtin_amdgcn_exp2f(-fabsf(r) * kLog2e);
-  const float w = 1.0f + e;
-  const float err = e - (w - 1.0f);
-  return (r > 0.0f ? r : 0.0f) + fmaf(__builtin_amdgcn_logf(w), kLn2, err);
+  return fmaf(__builtin_amdgcn_logf(1.0f + e), kLn2, r > 0.0f ? r : 0.0f);
 }
 
 __device__ __forceinline__ float silu_s(float z) {
@@ -63,35 +80,46 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
 // 8 consecutive bf16 from LDS (16-byte aligned)
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *(const bf16x8*)p; }
 
-// Q = 64 steps per chunk, N states (multiple of 32, <= 128), PS positions per workgroup
-// (16, 32 or 64).  MFMA lane layout (16x16x32): A row = lane%16, k = 8*(lane/16)+i;
-// B column = lane%16, k = 8*(lane/16)+i; D column = lane%16, rows 4*(lane/16)+r.
+// Operand fragment of a [k][r] bf16 array in LDS (row stride RS elements, a multiple of 4):
+// lane (l16, lq) receives rows k0 + 8 lq .. k0 + 8 lq + 7 of column r0 + l16.
+template <int RS>
+__device__ __forceinline__ bf16x8 ld8_tr(const uint16_t* base, int k0, int r0, int l16, int lq) {
+  const uint16_t* p0 = base + (k0 + 8 * lq + (l16 >> 2)) * RS + r0 + 4 * (l16 & 3);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+  const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * RS));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Q = 64 steps per chunk, N states (32, 64 or 128), PS positions per workgroup (16 or 32).
+// MFMA lane layout (16x16x32): A row = lane%16, k = 8*(lane/16)+i; B column = lane%16,
+// k = 8*(lane/16)+i; D column = lane%16, rows 4*(lane/16)+r.
 template <int N, int PS, bool ZOH>
-__global__ void __launch_bounds__(256) ssd_kernel(KParams p) {
+__global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   constexpr int Q = 64;
-  constexpr int NP = N + 8;        // padded LDS row of N bf16
-  constexpr int QP = Q + 8;        // padded LDS row of Q bf16
-  constexpr int UP = PS + 8;       // padded LDS row of PS bf16
-  constexpr int NT = N / 16, PT = PS / 16;          // 16-wide tiles along states / positions
-  constexpr int SPW = (NT * PT) / 4;                // state tiles per wave
-  static_assert((NT * PT) % 4 == 0, "state tiles must split over 4 waves");
+  constexpr int NP = N + 8;            // row stride of sB [s][n] and sH [p][n]
+  constexpr int XP = PS + 8;           // row stride of sX, sXW [s][p]
+  constexpr int MP = Q + 8;            // row stride of sM [t][s]
+  constexpr int NK = N / 32;           // 32-wide contraction steps over states
+  constexpr int PT = PS / 16;          // 16-wide position tiles
+  constexpr int NT = N / 16;           // 16-wide state tiles
+  constexpr int NST = NT * PT;         // state tiles of the slice
+  constexpr int SPW = (NST + 3) / 4;   // state tiles per wave (some waves may hold fewer)
+  constexpr int NBI = Q * N / 8 / 256; // 16-byte B items per thread
+  constexpr int NUI = Q * PS / 8;      // 16-byte u items of a chunk (threads below NUI own one)
+  static_assert(NBI >= 1 && NUI <= 256, "items per thread");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sC[Q * NP];     // C [t][n]
-  __shared__ __attribute__((aligned(16))) uint16_t sB[Q * NP];     // B [s][n]
-  __shared__ __attribute__((aligned(16))) uint16_t sBt[N * QP];    // B^T [n][s]
-  __shared__ __attribute__((aligned(16))) uint16_t sXt[PS * QP];   // (dt*u)^T [p][s], high part
-  __shared__ __attribute__((aligned(16))) uint16_t sXtl[PS * QP];  // its remainder
-  __shared__ __attribute__((aligned(16))) uint16_t sXWt[PS * QP];  // (w*dt*u)^T [p][s], w_s = exp(cum_end - cum_s)
-  __shared__ __attribute__((aligned(16))) uint16_t sXWtl[PS * QP]; // its remainder
-  __shared__ __attribute__((aligned(16))) uint16_t sM[4][16 * QP]; // per wave: its 16 rows of (L o C B^T), high
-  __shared__ __attribute__((aligned(16))) uint16_t sMl[4][16 * QP];// remainder
-  __shared__ __attribute__((aligned(16))) uint16_t sHt[PS * NP];   // state^T [p][n] (bf16 operand copy), high
-  __shared__ __attribute__((aligned(16))) uint16_t sHtl[PS * NP];  // remainder
-  __shared__ __attribute__((aligned(16))) uint16_t sU[Q * UP];    // u [t][p] (for the D*u skip)
-  __shared__ __attribute__((aligned(16))) uint16_t sZ[Q * UP];    // z [t][p] (for the gate)
-  __shared__ float sDt[Q], sCum[Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[Q * NP];         // B [s][n]
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][Q * XP];      // dt*u [s][p], hi / lo
+  __shared__ __attribute__((aligned(16))) uint16_t sXW[2][Q * XP];     // e^{cum_end - cum_s} dt*u, hi / lo
+  __shared__ __attribute__((aligned(16))) uint16_t sM[4][2][16 * MP];  // per wave: M^T of its 16 steps [t][s]
+  __shared__ __attribute__((aligned(16))) uint16_t sH[2][PS * NP];     // state [p][n], hi / lo
+  __shared__ float sCum[4][Q];                                         // per wave: cum (log2 units)
+  __shared__ float sDt[4][Q];                                          // per wave: step sizes
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lq = lane >> 4;
   const int pslice = blockIdx.x, hh = blockIdx.y, b = blockIdx.z;
   const int64_t L = p.L;
@@ -101,30 +129,33 @@ __global__ void __launch_bounds__(256) ssd_kernel(KParams p) {
   const float A2 = p.A[hh] * kLog2e;
   const float biash = p.bias ? p.bias[hh] : 0.0f;
 
-  // ---- the state: wave w holds state tiles k = w*SPW + i, tile k = (tn, tp) = (k / PT, k % PT);
-  //      element (n, q) = (16 tn + 4 lq + r, 16 tp + l16) of the (N x PS) state of this slice
+  // ---- the state: wave w holds state tiles k = w + 4 i (i < SPW, k < NST), tile k =
+  //      (tn, tp) = (k / PT, k % PT); element (n, q) = (16 tn + 4 lq + r, 16 tp + l16)
   f32x4 hs[SPW];
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
-    const int k = w * SPW + i, tn = k / PT, tp = k % PT;
+    const int k = w + 4 * i, tn = k / PT, tp = k % PT;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int n = 16 * tn + 4 * lq + r, q = 16 * tp + l16;
-      hs[i][r] = p.h0 ? p.h0[((int64_t)b * p.dim + (int64_t)hh * P + p0 + q) * N + n] : 0.0f;
+      hs[i][r] = (k < NST && p.h0) ? p.h0[((int64_t)b * p.dim + (int64_t)hh * P + p0 + q) * N + n] : 0.0f;
     }
   }
-  auto store_state_operand = [&]() {    // sHt[q][n] = bf16(state)
+  auto store_state = [&]() {   // sH[q][n..n+3] = split(state): 8-byte writes
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const int k = w * SPW + i, tn = k / PT, tp = k % PT;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int o = (16 * tp + l16) * NP + 16 * tn + 4 * lq + r;
-        split_bf(hs[i][r], sHt[o], sHtl[o]);
+      const int k = w + 4 * i, tn = k / PT, tp = k % PT;
+      if (k < NST) {
+        uint32_t h0, l0, h1, l1;
+        split2(hs[i][0], hs[i][1], h0, l0);
+        split2(hs[i][2], hs[i][3], h1, l1);
+        const int o = (16 * tp + l16) * NP + 16 * tn + 4 * lq;
+        *(u32x2*)&sH[0][o] = (u32x2){h0, h1};
+        *(u32x2*)&sH[1][o] = (u32x2){l0, l1};
       }
     }
   };
-  store_state_operand();
+  store_state();
 
   const uint16_t* const gB = (const uint16_t*)p.B;
   const uint16_t* const gC = (const uint16_t*)p.C;
@@ -132,31 +163,47 @@ __global__ void __launch_bounds__(256) ssd_kernel(KParams p) {
   const uint16_t* const gDt = (const uint16_t*)p.delta;
   const uint16_t* const gZ = (const uint16_t*)(p.z ? p.z : p.u);
   uint16_t* const gY = (uint16_t*)p.y;
+  const int64_t rowBC = (int64_t)G * N;          // elements between steps in B, C
+  const int64_t rowX = (int64_t)H * P;           // elements between steps in u, z, y
+  const int64_t colX = (int64_t)hh * P + p0;     // this slice's first position within a step
 
-  // ---- global loads of the next chunk, issued while the current one computes.  Every
-  // thread owns fixed items: B/C item k = (s, 8 states), u/z item k = (s, 8 positions),
-  // with s = (tid + 256 k) % Q.  Rows past the end of the sequence load the last valid
-  // row (an in-bounds address) and are zeroed when staged.
-  constexpr int NBI = Q * (N / 8) / 256, NUI = Q * (PS / 8) / 256;
-  static_assert(NBI >= 1 && NUI >= 1, "items per thread");
+  // D of this lane's output positions: 4 per position tile
+  float Dq[PT][4];
+#pragma unroll
+  for (int j = 0; j < PT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Dq[j][r] = p.D ? p.D[colX + 16 * j + 4 * lq + r] : 0.0f;
+
+  // ---- global loads of a chunk, issued one chunk ahead.  B items: (s, 8 states) per
+  // 16 bytes, NBI per thread; u items: (s, 8 positions); C fragments: this wave's 16 steps,
+  // 8 states per lane and contraction step; u and z of this lane's outputs; raw step size
+  // of step lane.  Steps past the end load the last valid step (in-bounds, masked later).
   const int64_t last_chunk = ((L - 1) / Q) * Q;
-  uint4 pB[NBI], pC[NBI], pU[NUI], pZ[NUI];
+  u32x4 pB[NBI], pC[NK], pU = {0u, 0u, 0u, 0u};
+  u32x2 pUo[PT], pZo[PT];
   float pDelta;
   auto prefetch = [&](int64_t tc) {
     const int nv = (int)min((int64_t)Q, L - tc);
+    const uint16_t* const bB = gB + ((int64_t)b * L + tc) * rowBC + (int64_t)g * N;
 #pragma unroll
     for (int k = 0; k < NBI; ++k) {
-      const int it = tid + 256 * k, s = min(it % Q, nv - 1), nb = (it / Q) * 8;
-      const int64_t gi = (((int64_t)b * L + tc + s) * G + g) * N + nb;
-      pB[k] = *(const uint4*)(gB + gi);
-      pC[k] = *(const uint4*)(gC + gi);
+      const int it = tid + 256 * k, s = min(it / (N / 8), nv - 1), nb = (it % (N / 8)) * 8;
+      pB[k] = *(const u32x4*)(bB + s * rowBC + nb);
     }
+    const int tC = min(16 * w + l16, nv - 1);
+    const uint16_t* const bC = gC + ((int64_t)b * L + tc + tC) * rowBC + (int64_t)g * N + 8 * lq;
 #pragma unroll
-    for (int k = 0; k < NUI; ++k) {
-      const int it = tid + 256 * k, s = min(it % Q, nv - 1), qb = (it / Q) * 8;
-      const int64_t gi = (((int64_t)b * L + tc + s) * H + hh) * P + p0 + qb;
-      pU[k] = *(const uint4*)(gU + gi);
-      pZ[k] = *(const uint4*)(gZ + gi);
+    for (int kk = 0; kk < NK; ++kk) pC[kk] = *(const u32x4*)(bC + 32 * kk);
+    const uint16_t* const bX = gU + ((int64_t)b * L + tc) * rowX + colX;
+    if (tid < NUI) {
+      const int s = min(tid / (PS / 8), nv - 1), qb = (tid % (PS / 8)) * 8;
+      pU = *(const u32x4*)(bX + s * rowX + qb);
+    }
+    const uint16_t* const bZ = gZ + ((int64_t)b * L + tc) * rowX + colX;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      pUo[j] = *(const u32x2*)(bX + tC * rowX + 16 * j + 4 * lq);
+      pZo[j] = *(const u32x2*)(bZ + tC * rowX + 16 * j + 4 * lq);
     }
     pDelta = bf2f(gDt[((int64_t)b * L + tc + min(lane, nv - 1)) * H + hh]);
   };
@@ -164,31 +211,23 @@ __global__ void __launch_bounds__(256) ssd_kernel(KParams p) {
 
   for (int64_t t0 = 0; t0 < L; t0 += Q) {
     const int nval = (int)min((int64_t)Q, L - t0);
-    // ================= phase 1: stage B, B^T, C, u, z, dt, cumulative decay, X ============
-    // (raw 16-bit words, not bf16 vector elements, so each element is addressed explicitly)
+    // ===== stage: B rows; this wave's step sizes and prefix sums; X and w X ===============
 #pragma unroll
     for (int k = 0; k < NBI; ++k) {
-      const int it = tid + 256 * k, s = it % Q, nb = (it / Q) * 8;
-      const bool ok = s < nval;
-      const uint4 bv = ok ? pB[k] : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 cv = ok ? pC[k] : make_uint4(0u, 0u, 0u, 0u);
-      *(uint4*)&sB[s * NP + nb] = bv;
-      *(uint4*)&sC[s * NP + nb] = cv;
-      const uint32_t wv[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sBt[(nb + 2 * i) * QP + s] = (uint16_t)(wv[i] & 0xffffu);
-        sBt[(nb + 2 * i + 1) * QP + s] = (uint16_t)(wv[i] >> 16);
-      }
+      const int it = tid + 256 * k, s = it / (N / 8), nb = (it % (N / 8)) * 8;
+      *(u32x4*)&sB[s * NP + nb] = pB[k];
     }
+    u32x4 cC[NK];
 #pragma unroll
-    for (int k = 0; k < NUI; ++k) {
-      const int it = tid + 256 * k, s = it % Q, qb = (it / Q) * 8;
-      const bool ok = s < nval;
-      *(uint4*)&sU[s * UP + qb] = ok ? pU[k] : make_uint4(0u, 0u, 0u, 0u);
-      *(uint4*)&sZ[s * UP + qb] = ok ? pZ[k] : make_uint4(0u, 0u, 0u, 0u);
+    for (int kk = 0; kk < NK; ++kk) cC[kk] = pC[kk];
+    u32x2 cUo[PT], cZo[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      cUo[j] = pUo[j];
+      cZo[j] = pZo[j];
     }
-    if (w == 0) {   // step sizes and their inclusive prefix sum (times A, log2 units)
+    const u32x4 cU = pU;
+    {   // every wave computes the chunk's step sizes and prefix sums itself (no barrier)
       float dt = 0.0f;
       if (lane < nval) {
         const float r = pDelta + biash;
@@ -200,131 +239,138 @@ __global__ void __launch_bounds__(256) ssd_kernel(KParams p) {
         const float v = __shfl_up(c, o);
         if (lane >= o) c += v;
       }
-      sDt[lane] = dt;
-      sCum[lane] = c * A2;        // log2 of the decay from the chunk start through step lane
+      sDt[w][lane] = dt;
+      sCum[w][lane] = c * A2;     // log2 of the decay from the chunk start through step lane
     }
-    __syncthreads();
-    const float cum_end = sCum[Q - 1];
-    // X^T and (w X)^T from this thread's u items (zero past the end)
-#pragma unroll
-    for (int k = 0; k < NUI; ++k) {
-      const int it = tid + 256 * k, s = it % Q, qb = (it / Q) * 8;
-      float dts = sDt[s];
+    // the next chunk's loads fly while this one computes (the last chunk re-reads itself)
+    prefetch(min(t0 + Q, last_chunk));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float cum_end = sCum[w][Q - 1];
+    if (tid < NUI) {   // X = dt u and w X of one u item, split into hi / lo
+      const int s = tid / (PS / 8), qb = (tid % (PS / 8)) * 8;
+      float dts = sDt[w][s];
       if (ZOH) {   // exact hold per head: dt -> expm1(x)/x * dt, x = dt*A
         const float y = dts * A2, x = y * kLn2;
         const float poly = fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 120.0f, 1.0f / 24.0f), 1.0f / 6.0f), 0.5f), 1.0f);
         dts *= fabsf(x) < 0.125f ? poly : (__builtin_amdgcn_exp2f(y) - 1.0f) * __builtin_amdgcn_rcpf(x);
       }
-      const float ws = __builtin_amdgcn_exp2f(cum_end - sCum[s]);
-      const uint4 uv = s < nval ? pU[k] : make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t wu[4] = {uv.x, uv.y, uv.z, uv.w};
+      const float ws = __builtin_amdgcn_exp2f(cum_end - sCum[w][s]);
+      uint32_t xh[4], xl[4], wh[4], wl[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = dts * bf2f((uint16_t)((i & 1) ? (wu[i >> 1] >> 16) : (wu[i >> 1] & 0xffffu)));
-        split_bf(x, sXt[(qb + i) * QP + s], sXtl[(qb + i) * QP + s]);
-        split_bf(x * ws, sXWt[(qb + i) * QP + s], sXWtl[(qb + i) * QP + s]);
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = dts * bf2f(cU[i] & 0xffffu), x1 = dts * bf2f(cU[i] >> 16);
+        split2(x0, x1, xh[i], xl[i]);
+        split2(x0 * ws, x1 * ws, wh[i], wl[i]);
       }
+      *(u32x4*)&sX[0][s * XP + qb] = (u32x4){xh[0], xh[1], xh[2], xh[3]};
+      *(u32x4*)&sX[1][s * XP + qb] = (u32x4){xl[0], xl[1], xl[2], xl[3]};
+      *(u32x4*)&sXW[0][s * XP + qb] = (u32x4){wh[0], wh[1], wh[2], wh[3]};
+      *(u32x4*)&sXW[1][s * XP + qb] = (u32x4){wl[0], wl[1], wl[2], wl[3]};
     }
-    __syncthreads();
-    // next chunk's loads fly while this one computes (the last chunk re-reads itself)
-    prefetch(min(t0 + Q, last_chunk));
+    __syncthreads();   // sB, sX, sXW of this chunk and sH of the previous one are complete
 
-    // ================= phase 2a: wave w owns output rows t in [16w, 16w+16) ===============
+    // ===== wave w: output steps t in [16w, 16w+16) =========================================
+    const int ks = 32 * ((w + 2) / 2);   // contraction range over steps covering s <= 16w+15
     {
-      const int tr = 16 * w;
-      // G = C B^T for column tiles j <= w, masked and decayed into this wave's rows of M
+      // M^T = (B C^T) o decay for the step tiles i <= w of this wave's column tile (zeros
+      // for i > w inside the range ks), stored [t][s] with 8-byte writes (wave-private)
+      const int t = 16 * w + l16;
+      const float cum_t = sCum[w][t];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j > w) {   // zero tile (s > t) inside the K range that Y_diag reads
-          if (j < 2 * ((w + 2) / 2)) {
+      for (int i = 0; i < 4; ++i) {
+        if (16 * i >= ks) continue;
+        uint32_t h0 = 0, l0 = 0, h1 = 0, l1 = 0;
+        if (i <= w) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sM[w][(4 * lq + r) * QP + 16 * j + l16] = sMl[w][(4 * lq + r) * QP + 16 * j + l16] = 0;
+          for (int kk = 0; kk < NK; ++kk)
+            acc = mfma(ld8(&sB[(16 * i + l16) * NP + 32 * kk + 8 * lq]), __builtin_bit_cast(bf16x8, cC[kk]), acc);
+          float m[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int s = 16 * i + 4 * lq + r;
+            m[r] = s <= t ? acc[r] * __builtin_amdgcn_exp2f(cum_t - sCum[w][s]) : 0.0f;
           }
-          continue;
+          split2(m[0], m[1], h0, l0);
+          split2(m[2], m[3], h1, l1);
         }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < N; kk += 32) {
-          const bf16x8 a = ld8(&sC[(tr + l16) * NP + kk + 8 * lq]);
-          const bf16x8 bb = ld8(&sB[(16 * j + l16) * NP + kk + 8 * lq]);
-          acc = mfma(a, bb, acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = tr + 4 * lq + r, s = 16 * j + l16;
-          const float m = s <= t ? acc[r] * __builtin_amdgcn_exp2f(sCum[t] - sCum[s]) : 0.0f;
-          split_bf(m, sM[w][(4 * lq + r) * QP + s], sMl[w][(4 * lq + r) * QP + s]);
-        }
+        const int o = l16 * MP + 16 * i + 4 * lq;
+        *(u32x2*)&sM[w][0][o] = (u32x2){h0, h1};
+        *(u32x2*)&sM[w][1][o] = (u32x2){l0, l1};
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // Y = M X (steps s <= t) and C H (from the entering state), per 16-position tile
-      const int ks = 32 * ((w + 2) / 2);                     // K range covering s <= 16w+15
+
+      // Y^T = X^T M^T + H^T C^T per position tile; lane: step t, positions 16 j + 4 lq + r
+      const float et = __builtin_amdgcn_exp2f(cum_t);
 #pragma unroll
-      for (int tp = 0; tp < PT; ++tp) {
+      for (int j = 0; j < PT; ++j) {
         f32x4 yd = {0.f, 0.f, 0.f, 0.f}, yo = {0.f, 0.f, 0.f, 0.f};
         for (int kk = 0; kk < ks; kk += 32) {
-          const bf16x8 a = ld8(&sM[w][l16 * QP + kk + 8 * lq]);
-          const bf16x8 al = ld8(&sMl[w][l16 * QP + kk + 8 * lq]);
-          const bf16x8 bb = ld8(&sXt[(16 * tp + l16) * QP + kk + 8 * lq]);
-          const bf16x8 bl = ld8(&sXtl[(16 * tp + l16) * QP + kk + 8 * lq]);
-          yd = mfma(a, bb, yd);
-          yd = mfma(a, bl, yd);
-          yd = mfma(al, bb, yd);
+          const bf16x8 xa = ld8_tr<XP>(sX[0], kk, 16 * j, l16, lq);
+          const bf16x8 xl = ld8_tr<XP>(sX[1], kk, 16 * j, l16, lq);
+          const bf16x8 mb = ld8(&sM[w][0][l16 * MP + kk + 8 * lq]);
+          const bf16x8 ml = ld8(&sM[w][1][l16 * MP + kk + 8 * lq]);
+          yd = mfma(xa, mb, yd);
+          yd = mfma(xa, ml, yd);
+          yd = mfma(xl, mb, yd);
         }
 #pragma unroll
-        for (int kk = 0; kk < N; kk += 32) {
-          const bf16x8 a = ld8(&sC[(tr + l16) * NP + kk + 8 * lq]);
-          const bf16x8 bb = ld8(&sHt[(16 * tp + l16) * NP + kk + 8 * lq]);
-          const bf16x8 bl = ld8(&sHtl[(16 * tp + l16) * NP + kk + 8 * lq]);
-          yo = mfma(a, bb, yo);
-          yo = mfma(a, bl, yo);
+        for (int kk = 0; kk < NK; ++kk) {
+          const bf16x8 c = __builtin_bit_cast(bf16x8, cC[kk]);
+          yo = mfma(ld8(&sH[0][(16 * j + l16) * NP + 32 * kk + 8 * lq]), c, yo);
+          yo = mfma(ld8(&sH[1][(16 * j + l16) * NP + 32 * kk + 8 * lq]), c, yo);
         }
-        // epilogue: y = Yd + e^{cum_t} Yo + D u, gated; column q = 16 tp + l16, rows t = tr + 4 lq + r
-        const int q = 16 * tp + l16;
-        const float Dq = p.D ? p.D[(int64_t)hh * P + p0 + q] : 0.0f;
+        // y = Yd + e^{cum_t} Yo + D u, gated: 4 consecutive positions of step t
+        const uint32_t u01 = cUo[j][0], u23 = cUo[j][1], z01 = cZo[j][0], z23 = cZo[j][1];
+        const float uv[4] = {bf2f(u01 & 0xffffu), bf2f(u01 >> 16), bf2f(u23 & 0xffffu), bf2f(u23 >> 16)};
+        const float zv[4] = {bf2f(z01 & 0xffffu), bf2f(z01 >> 16), bf2f(z23 & 0xffffu), bf2f(z23 >> 16)};
+        float yv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = tr + 4 * lq + r;
-          if (t < nval) {
-            const int64_t gi = (((int64_t)b * L + t0 + t) * H + hh) * P + p0 + q;
-            float yv = yd[r] + __builtin_amdgcn_exp2f(sCum[t]) * yo[r] + Dq * bf2f(sU[t * UP + q]);
-            if (p.z) yv *= silu_s(bf2f(sZ[t * UP + q]));
-            gY[gi] = f2bf(yv);
-          }
+          yv[r] = fmaf(et, yo[r], yd[r]) + Dq[j][r] * uv[r];
+          if (p.z) yv[r] *= silu_s(zv[r]);
+        }
+        if (t < nval) {
+          const u32x2 o = {pack_bf(yv[0], yv[1]), pack_bf(yv[2], yv[3])};
+          __builtin_nontemporal_store(o, (u32x2*)(gY + ((int64_t)b * L + t0 + t) * rowX + colX + 16 * j + 4 * lq));
         }
       }
     }
-    // ================= phase 2b: the chunk's state contribution, then the new state ======
+    // ===== the chunk's state contribution S = B^T (w X), then the new state ================
+    const float dec = __builtin_amdgcn_exp2f(cum_end);
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const int k = w * SPW + i, tn = k / PT, tp = k % PT;
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      const int k = w + 4 * i, tn = k / PT, tp = k % PT;
+      if (k < NST) {
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < Q; kk += 32) {
-        const bf16x8 a = ld8(&sBt[(16 * tn + l16) * QP + kk + 8 * lq]);
-        const bf16x8 bb = ld8(&sXWt[(16 * tp + l16) * QP + kk + 8 * lq]);
-        const bf16x8 bl = ld8(&sXWtl[(16 * tp + l16) * QP + kk + 8 * lq]);
-        sacc = mfma(a, bb, sacc);
-        sacc = mfma(a, bl, sacc);
+        for (int kk = 0; kk < Q; kk += 32) {
+          const bf16x8 a = ld8_tr<NP>(sB, kk, 16 * tn, l16, lq);
+          sacc = mfma(a, ld8_tr<XP>(sXW[0], kk, 16 * tp, l16, lq), sacc);
+          sacc = mfma(a, ld8_tr<XP>(sXW[1], kk, 16 * tp, l16, lq), sacc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hs[i][r] = fmaf(dec, hs[i][r], sacc[r]);
       }
-      const float dec = __builtin_amdgcn_exp2f(cum_end);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) hs[i][r] = fmaf(dec, hs[i][r], sacc[r]);
     }
-    __syncthreads();       // every wave is done with this chunk's buffers and the old state copy
-    store_state_operand();
+    __syncthreads();   // every wave is done with this chunk's sB, sX, sXW and the old sH
+    store_state();
   }
   // ---- final state
   if (p.h_last) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const int k = w * SPW + i, tn = k / PT, tp = k % PT;
+      const int k = w + 4 * i, tn = k / PT, tp = k % PT;
+      if (k < NST) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = 16 * tn + 4 * lq + r, q = 16 * tp + l16;
-        p.h_last[((int64_t)b * p.dim + (int64_t)hh * P + p0 + q) * N + n] = hs[i][r];
+        for (int r = 0; r < 4; ++r) {
+          const int n = 16 * tn + 4 * lq + r, q = 16 * tp + l16;
+          p.h_last[((int64_t)b * p.dim + colX + q) * N + n] = hs[i][r];
+        }
       }
     }
   }
@@ -341,15 +387,15 @@ int launch_ps(const KParams& kp, int zoh, hipStream_t st) {
 template <int N>
 int launch_n(const KParams& kp, int ps, int zoh, hipStream_t st) {
   switch (ps) {
-    case 64: return launch_ps<N, 64>(kp, zoh, st);
     case 32: return launch_ps<N, 32>(kp, zoh, st);
+    case 16: return launch_ps<N, 16>(kp, zoh, st);
     default: return (int)hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-// N in {32, 64, 128}; ps (positions per workgroup) in {32, 64} and divides P.
+// N in {32, 64, 128}; ps (positions per workgroup) in {16, 32} and divides P.
 int launch_ssd(const KParams& kp, int ps, int zoh, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   switch (kp.N) {

@@ -54,6 +54,9 @@ CASES = [
     dict(seqlen=300, dim=256, dstate=32, nheads=4, headdim=64, ngroups=2, has_z=False),
     dict(seqlen=257, dim=128, dstate=128, nheads=2, headdim=64, has_h0=False, has_D=False),
     dict(seqlen=190, dim=128, dstate=64, nheads=2, headdim=64, delta_kind="wide", has_bias=False),
+    dict(seqlen=130, dim=96, dstate=64, nheads=2, headdim=48),          # 16 positions per workgroup
+    dict(seqlen=70, dim=64, dstate=32, nheads=4, headdim=16),
+    dict(seqlen=129, dim=64, dstate=128, nheads=1, headdim=64, ngroups=1),
 ]
 
 
@@ -98,3 +101,19 @@ def test_ssd_agrees_with_scan_kernel(monkeypatch):
     monkeypatch.setenv("SSM_SCAN_SSD", "0")
     y2, h2 = gpu_run(c)
     assert err(y1, y2.double().cpu().numpy()) <= TOL and err(h1, h2.double().cpu().numpy()) <= TOL
+
+
+@pytest.mark.parametrize("dstate", [32, 128])
+def test_ssd_sixteen_positions_per_workgroup(dstate, monkeypatch):
+    """The 16-position slices (forced) against the oracle and against the 32-position ones."""
+    c = make_case("ssd4", layout="blhp", io_dtype="bf16", batch=2, seqlen=321, dim=128, dstate=dstate, nheads=2,
+                  headdim=64, seed=17 + dstate, has_h0=True, A_kind="head_uniform")
+    y1, h1 = gpu_run(c)
+    monkeypatch.setenv("SSM_SSD_PS", "16")
+    dims = scan.make_dims("blhp", "bf16", c.batch, c.seqlen, c.dim, c.dstate, c.nheads, c.headdim, c.ngroups)
+    assert "kernel=ssd" in scan.describe(dims) and "grid=(4," in scan.describe(dims)
+    print("[gpu] ssd 16 positions per workgroup", flush=True)
+    y2, h2 = gpu_run(c)
+    y_ref, h_ref = oracle_run(c)
+    assert err(y2, y_ref) <= TOL and err(h2, h_ref) <= TOL
+    assert err(y2, y1.double().cpu().numpy()) <= TOL and err(h2, h1.double().cpu().numpy()) <= TOL
