@@ -73,6 +73,13 @@ __device__ __forceinline__ float silu_s(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
+// x taken from another lane by a DPP pattern; lanes without a source (or in rows outside
+// ROWS) read 0
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, true));
+}
+
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -98,9 +105,14 @@ __device__ __forceinline__ bf16x8 ld8_tr(const uint16_t* base, int k0, int r0, i
 template <int N, int PS, bool ZOH>
 __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   constexpr int Q = 64;
-  constexpr int NP = N + 8;            // row stride of sB [s][n] and sH [p][n]
-  constexpr int XP = PS + 8;           // row stride of sX, sXW [s][p]
-  constexpr int MP = Q + 8;            // row stride of sM [t][s]
+  // Row strides (elements).  With 16-lane passes, a row stride of 16 B times an odd number
+  // keeps the 16 rows of a 16-byte fragment read on distinct banks, and 7, 9 or 19 times
+  // 16 B also keeps the 4 rows x 32 B of a transposing read apart.
+  constexpr int BP = N == 32 ? 56 : N == 64 ? 72 : 152;   // sB [s][n]: read plainly and transposed
+  constexpr int NP = N + 8;            // sH [p][n]: plain reads only
+  constexpr int XP = PS == 16 ? 56 : 72;   // sX, sXW [s][hi p | lo p]: transposed reads
+  constexpr int MP = Q + 8;            // sM [t][s]
+  static_assert(BP >= N && XP >= 2 * PS, "row strides");
   constexpr int NK = N / 32;           // 32-wide contraction steps over states
   constexpr int PT = PS / 16;          // 16-wide position tiles
   constexpr int NT = N / 16;           // 16-wide state tiles
@@ -110,9 +122,9 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   constexpr int NUI = Q * PS / 8;      // 16-byte u items of a chunk (threads below NUI own one)
   static_assert(NBI >= 1 && NUI <= 256, "items per thread");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sB[Q * NP];         // B [s][n]
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][Q * XP];      // dt*u [s][p], hi / lo
-  __shared__ __attribute__((aligned(16))) uint16_t sXW[2][Q * XP];     // e^{cum_end - cum_s} dt*u, hi / lo
+  __shared__ __attribute__((aligned(16))) uint16_t sB[Q * BP];         // B [s][n]
+  __shared__ __attribute__((aligned(16))) uint16_t sX[Q * XP];         // dt*u [s][hi p | lo p]
+  __shared__ __attribute__((aligned(16))) uint16_t sXW[Q * XP];        // e^{cum_end - cum_s} dt*u, same
   __shared__ __attribute__((aligned(16))) uint16_t sM[4][2][16 * MP];  // per wave: M^T of its 16 steps [t][s]
   __shared__ __attribute__((aligned(16))) uint16_t sH[2][PS * NP];     // state [p][n], hi / lo
   __shared__ float sCum[4][Q];                                         // per wave: cum (log2 units)
@@ -215,7 +227,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
 #pragma unroll
     for (int k = 0; k < NBI; ++k) {
       const int it = tid + 256 * k, s = it / (N / 8), nb = (it % (N / 8)) * 8;
-      *(u32x4*)&sB[s * NP + nb] = pB[k];
+      *(u32x4*)&sB[s * BP + nb] = pB[k];
     }
     u32x4 cC[NK];
 #pragma unroll
@@ -233,12 +245,15 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
         const float r = pDelta + biash;
         dt = p.softplus ? softplus_s(r) : r;
       }
+      // inclusive prefix sum over the 64 lanes with DPP (no LDS round trips): shifts within
+      // rows of 16, then the last lane of row 0 / rows 0-1 broadcast into the rows above
       float c = dt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float v = __shfl_up(c, o);
-        if (lane >= o) c += v;
-      }
+      c += dpp_f<0x111, 0xf>(c);   // row_shr:1
+      c += dpp_f<0x112, 0xf>(c);   // row_shr:2
+      c += dpp_f<0x114, 0xf>(c);   // row_shr:4
+      c += dpp_f<0x118, 0xf>(c);   // row_shr:8
+      c += dpp_f<0x142, 0xa>(c);   // row_bcast:15 into rows 1 and 3
+      c += dpp_f<0x143, 0xc>(c);   // row_bcast:31 into rows 2 and 3
       sDt[w][lane] = dt;
       sCum[w][lane] = c * A2;     // log2 of the decay from the chunk start through step lane
     }
@@ -264,10 +279,10 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
         split2(x0, x1, xh[i], xl[i]);
         split2(x0 * ws, x1 * ws, wh[i], wl[i]);
       }
-      *(u32x4*)&sX[0][s * XP + qb] = (u32x4){xh[0], xh[1], xh[2], xh[3]};
-      *(u32x4*)&sX[1][s * XP + qb] = (u32x4){xl[0], xl[1], xl[2], xl[3]};
-      *(u32x4*)&sXW[0][s * XP + qb] = (u32x4){wh[0], wh[1], wh[2], wh[3]};
-      *(u32x4*)&sXW[1][s * XP + qb] = (u32x4){wl[0], wl[1], wl[2], wl[3]};
+      *(u32x4*)&sX[s * XP + qb] = (u32x4){xh[0], xh[1], xh[2], xh[3]};
+      *(u32x4*)&sX[s * XP + PS + qb] = (u32x4){xl[0], xl[1], xl[2], xl[3]};
+      *(u32x4*)&sXW[s * XP + qb] = (u32x4){wh[0], wh[1], wh[2], wh[3]};
+      *(u32x4*)&sXW[s * XP + PS + qb] = (u32x4){wl[0], wl[1], wl[2], wl[3]};
     }
     __syncthreads();   // sB, sX, sXW of this chunk and sH of the previous one are complete
 
@@ -286,7 +301,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < NK; ++kk)
-            acc = mfma(ld8(&sB[(16 * i + l16) * NP + 32 * kk + 8 * lq]), __builtin_bit_cast(bf16x8, cC[kk]), acc);
+            acc = mfma(ld8(&sB[(16 * i + l16) * BP + 32 * kk + 8 * lq]), __builtin_bit_cast(bf16x8, cC[kk]), acc);
           float m[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -310,8 +325,8 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
       for (int j = 0; j < PT; ++j) {
         f32x4 yd = {0.f, 0.f, 0.f, 0.f}, yo = {0.f, 0.f, 0.f, 0.f};
         for (int kk = 0; kk < ks; kk += 32) {
-          const bf16x8 xa = ld8_tr<XP>(sX[0], kk, 16 * j, l16, lq);
-          const bf16x8 xl = ld8_tr<XP>(sX[1], kk, 16 * j, l16, lq);
+          const bf16x8 xa = ld8_tr<XP>(sX, kk, 16 * j, l16, lq);
+          const bf16x8 xl = ld8_tr<XP>(sX, kk, PS + 16 * j, l16, lq);
           const bf16x8 mb = ld8(&sM[w][0][l16 * MP + kk + 8 * lq]);
           const bf16x8 ml = ld8(&sM[w][1][l16 * MP + kk + 8 * lq]);
           yd = mfma(xa, mb, yd);
@@ -349,9 +364,9 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < Q; kk += 32) {
-          const bf16x8 a = ld8_tr<NP>(sB, kk, 16 * tn, l16, lq);
-          sacc = mfma(a, ld8_tr<XP>(sXW[0], kk, 16 * tp, l16, lq), sacc);
-          sacc = mfma(a, ld8_tr<XP>(sXW[1], kk, 16 * tp, l16, lq), sacc);
+          const bf16x8 a = ld8_tr<BP>(sB, kk, 16 * tn, l16, lq);
+          sacc = mfma(a, ld8_tr<XP>(sXW, kk, 16 * tp, l16, lq), sacc);
+          sacc = mfma(a, ld8_tr<XP>(sXW, kk, PS + 16 * tp, l16, lq), sacc);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) hs[i][r] = fmaf(dec, hs[i][r], sacc[r]);
