@@ -150,28 +150,52 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
     p.bc_bytes = (size_t)d->batch * (size_t)d->ngroups * (size_t)p.nblk * (size_t)p.TB * 2 * (size_t)p.Npad *
                  sizeof(float);
     p.bc_bytes = (p.bc_bytes + 255) & ~(size_t)255;
-    // 16 states in one segment: an 80-channel launch (one workgroup per CU, the same
-    // work on every SIMD) when its busiest SIMD has less to do than the plain launch's.
-    // A workgroup costs about 2.6 plain waves of work per SIMD.  SSM_SCAN_MIXED=0/1
-    // forces the choice (tests, tuning).  The 80-channel launch is the mixed one with 4
-    // and 16 lanes per channel (independent waves, two per SIMD); SSM_SCAN_MIXED4=0 gives
-    // 8 and 16 lanes per channel (three waves per SIMD), SSM_SCAN_SPLIT=4 or 2 the split
-    // one (states over waves, 4 or 2 per wave, B/C in scalar registers, two workgroup
-    // barriers per block; its tiles take twice the workspace).  Both measured slower on
+    // 16 states: an 80-channel launch (one workgroup per CU per segment, the same work on
+    // every SIMD) when its busiest SIMD has less to do than the plain launch's, over the
+    // main pass and (with time segments) the aggregate pass, which costs about 0.7 of a
+    // main pass per step.  A workgroup costs about 2.6 plain waves of work per SIMD.  The
+    // 80-channel launch picks its own segment count.  SSM_SCAN_MIXED=0/1 forces the choice
+    // (tests, tuning).  The 80-channel launch is the mixed one with 4 and 16 lanes per
+    // channel (independent waves, two per SIMD); SSM_SCAN_MIXED4=0 gives 8 and 16 lanes per
+    // channel (three waves per SIMD), SSM_SCAN_SPLIT=4 or 2 the split one (states over
+    // waves, 4 or 2 per wave, B/C in scalar registers, two workgroup barriers per block,
+    // one segment only; its tiles take twice the workspace).  Both measured slower on
     // MI355X: the first spends more instructions and LDS traffic per element, the second
     // stalls at its barriers.
-    if (allow_mixed && p.Npad == 16 && p.nseg == 1) {
+    if (allow_mixed && p.Npad == 16) {
+      const char* senv = std::getenv("SSM_SCAN_SPLIT");
+      const bool split = senv && (*senv == '2' || *senv == '4');
+      const char* seg_env = std::getenv("SSM_SCAN_SEGMENTS");
+      const bool seg_forced = seg_env && *seg_env;
+      const int64_t L = d->seqlen;
+      auto pass_cost = [&](int64_t units, int64_t slots, int64_t nseg, double unit_cost) {
+        const int64_t len = (int64_t)round_up((L + nseg - 1) / nseg, p.TB);
+        const int64_t ns = (L + len - 1) / len;
+        const double main = (double)((units * ns + slots - 1) / slots);
+        const double agg = ns > 1 ? (double)((units * (ns - 1) + slots - 1) / slots) : 0.0;
+        return unit_cost * (main + 0.7 * agg) * (double)len;
+      };
       const int64_t mixed_blocks = (rows_per_group + 79) / 80;
       const int64_t wgs = mixed_blocks * groups_or_heads * d->batch;
       const int64_t waves = (int64_t)p.blocks_per_group * groups_or_heads * d->batch;
-      const double cost_mixed = 2.6 * (double)((wgs + kCUs - 1) / kCUs);
-      const double cost_plain = (double)((waves + 4 * kCUs - 1) / (4 * kCUs));
+      const double cost_plain = pass_cost(waves, 4 * kCUs, p.nseg, 1.0);
+      int64_t best_nseg = 1;
+      double cost_mixed = pass_cost(wgs, kCUs, 1, 2.6);
+      if (seg_forced) {
+        best_nseg = p.nseg;
+        cost_mixed = pass_cost(wgs, kCUs, best_nseg, 2.6);
+      } else if (!split) {
+        const int64_t max_seg = std::min<int64_t>(65535, (L + 255) / 256);
+        for (int64_t ns = 2; ns <= std::min<int64_t>(max_seg, 64); ++ns) {
+          const double c = pass_cost(wgs, kCUs, ns, 2.6);
+          if (c < cost_mixed) { cost_mixed = c; best_nseg = ns; }
+        }
+      }
       bool mixed = cost_mixed < cost_plain;
       const char* env = std::getenv("SSM_SCAN_MIXED");
       if (env && *env) mixed = *env != '0';
+      if (split && best_nseg != 1) mixed = false;   // the split launch runs one segment
       if (mixed && groups_or_heads * mixed_blocks <= 0x7fffffff) {
-        const char* senv = std::getenv("SSM_SCAN_SPLIT");
-        const bool split = senv && (*senv == '2' || *senv == '4');
         const char* m4env = std::getenv("SSM_SCAN_MIXED4");
         const bool mixed4 = !(m4env && *m4env == '0');
         p.kernel = split ? 4 : mixed4 ? 5 : 3;
@@ -181,6 +205,14 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
         p.blocks_per_group = (int)mixed_blocks;
         p.grid_rows = (int)(groups_or_heads * mixed_blocks);
         if (p.kernel == 4) p.bc_bytes *= 2;
+        if (best_nseg != p.nseg) {   // the 80-channel launch's own segment count
+          int64_t len = round_up((L + best_nseg - 1) / best_nseg, p.TB);
+          p.seg_len = len;
+          p.nseg = (int)((L + len - 1) / len);
+          p.seg_bytes = p.nseg > 1 ? (size_t)2 * (size_t)(p.nseg - 1) * (size_t)d->batch * (size_t)p.Npad *
+                                         (size_t)d->dim * sizeof(float)
+                                   : 0;
+        }
       }
     }
   }

@@ -1411,8 +1411,15 @@ int launch_rowgroup_mixed(const KParams& kp, hipStream_t st) {
   hipLaunchKernelGGL((bc_tile_kernel<IO, 16>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL((rowgroup_mixed_kernel<IO, 0, VECOK>), dim3(kp.blocks_per_group * kp.G, kp.batch, 1),
-                     dim3(rg::MIX_WAVES * 64), 0, st, kp);
+  const int gx = kp.blocks_per_group * kp.G;
+  if (kp.nseg > 1) {
+    hipLaunchKernelGGL((rowgroup_mixed_kernel<IO, 1, VECOK>), dim3(gx, kp.batch, kp.nseg - 1),
+                       dim3(rg::MIX_WAVES * 64), 0, st, kp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  hipLaunchKernelGGL((rowgroup_mixed_kernel<IO, 0, VECOK>), dim3(gx, kp.batch, kp.nseg), dim3(rg::MIX_WAVES * 64), 0,
+                     st, kp);
   return (int)hipGetLastError();
 }
 
@@ -1431,8 +1438,15 @@ int launch_rowgroup_mixed4_f(const KParams& kp, hipStream_t st) {
   hipLaunchKernelGGL((bc_tile_kernel<IO, 16>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL((rowgroup_mixed4_kernel<IO, 0, VECOK, SPF, HZF>), dim3(kp.blocks_per_group * kp.G, kp.batch, 1),
-                     dim3(8 * 64), 0, st, kp);
+  const int gx = kp.blocks_per_group * kp.G;
+  if (kp.nseg > 1) {   // aggregates of the segments before the last, then the main pass folds them
+    hipLaunchKernelGGL((rowgroup_mixed4_kernel<IO, 1, VECOK, SPF, HZF>), dim3(gx, kp.batch, kp.nseg - 1),
+                       dim3(8 * 64), 0, st, kp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  hipLaunchKernelGGL((rowgroup_mixed4_kernel<IO, 0, VECOK, SPF, HZF>), dim3(gx, kp.batch, kp.nseg), dim3(8 * 64), 0,
+                     st, kp);
   return (int)hipGetLastError();
 }
 

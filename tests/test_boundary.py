@@ -134,8 +134,9 @@ def test_workspace_size_and_plan():
     assert "kernel=rowgroup " in scan.describe(d2) and "grid=(48,8,1)" in scan.describe(d2)
     d32 = dims(batch=4, seqlen=2048, dim=5120, dstate=32)             # 32 states: plain
     assert "kernel=rowgroup " in scan.describe(d32)
-    d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # 40 row blocks: segmented
-    assert scan.workspace_size(d4) > 0
+    d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # 32 workgroups: 8 time segments
+    assert scan.workspace_size(d4) == bc_tile_bytes(1, 131072, 16) + 2 * 7 * 1 * 16 * 2560 * 4
+    assert "kernel=rowgroup_mixed4" in scan.describe(d4) and "grid=(32,1,8)" in scan.describe(d4)
     d5 = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
     assert "kernel=ssd" in scan.describe(d5) and scan.workspace_size(d5) == 0
     d5f = scan.make_dims("blhp", "f32", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
@@ -250,5 +251,10 @@ def test_mixed_launch_override_env(monkeypatch):
     monkeypatch.setenv("SSM_SCAN_SPLIT", "4")
     assert "kernel=rowgroup_split" in scan.describe(d2) and "states_per_wave=4" in scan.describe(d2)
     assert scan.workspace_size(d) == 2 * ws                             # two tile layouts
-    d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # segmented: never mixed
-    assert "kernel=rowgroup " in scan.describe(d4)
+    d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # the split launch: one segment
+    assert "kernel=rowgroup_split" in scan.describe(d4) and "grid=(32,1,1)" in scan.describe(d4)
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", "3")                      # forced segments: not the split launch
+    assert "kernel=rowgroup " in scan.describe(d4) and "grid=(80,1,3)" in scan.describe(d4)
+    monkeypatch.setenv("SSM_SCAN_SPLIT", "0")
+    monkeypatch.setenv("SSM_SCAN_MIXED4", "1")
+    assert "kernel=rowgroup_mixed4" in scan.describe(d4) and "grid=(32,1,3)" in scan.describe(d4)

@@ -230,6 +230,23 @@ def test_mixed_launch(io, D, L, G, launch, monkeypatch):
     check_case(c)
 
 
+@pytest.mark.parametrize("launch", ["mixed4", "mixed"])
+@pytest.mark.parametrize("L,nseg", [(1000, "3"), (97, "3"), (4100, "5")])
+def test_mixed_launch_segments(L, nseg, launch, monkeypatch):
+    """The 80-channel launches over time segments: an aggregate pass per segment before the
+    last, then the main pass folding them into each segment's initial state."""
+    env, kname, _ = LAUNCH16[launch]
+    monkeypatch.setenv("SSM_SCAN_MIXED", "1")
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", nseg)
+    c = make_case("mixed_seg", layout="bdl", io_dtype="bf16", batch=2, seqlen=L, dim=170, dstate=16,
+                  seed=L + 3, has_h0=True, A_kind="lognormal")
+    txt = scan.describe(scan.make_dims("bdl", "bf16", 2, L, 170, 16))
+    assert kname in txt and ",2,1)" not in txt
+    check_case(c)
+
+
 @pytest.mark.parametrize("launch", list(LAUNCH16))
 @pytest.mark.parametrize("opts", [dict(has_z=False), dict(has_D=False, has_bias=False), dict(delta_kind="wide"),
                                   dict(softplus=False, delta_kind="zero")])
