@@ -62,6 +62,7 @@ __device__ __forceinline__ float zoh_factor(float y, float a) {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- element I/O
@@ -153,7 +154,13 @@ struct BF16IO {
   }
   template <int V> __device__ static void stv_stream(void* p, const float* v) {
     const bf16x2 a = {(__bf16)v[0], (__bf16)v[1]};
-    if constexpr (V == 4) {
+    if constexpr (V == 8) {
+      const bf16x2 c = {(__bf16)v[2], (__bf16)v[3]}, e = {(__bf16)v[4], (__bf16)v[5]},
+                   f = {(__bf16)v[6], (__bf16)v[7]};
+      const u32x4 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, e),
+                       __builtin_bit_cast(uint32_t, f)};
+      __builtin_nontemporal_store(w, (u32x4*)p);
+    } else if constexpr (V == 4) {
       const bf16x2 c = {(__bf16)v[2], (__bf16)v[3]};
       const u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
       __builtin_nontemporal_store(w, (u32x2*)p);
@@ -926,8 +933,8 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
       char* const yb = py + tb * kB;
       if (VECOK && nvalid == TB) {
 #pragma unroll
-        for (int q = 0; q < QPL; q += (QPL < 4 ? QPL : 4))
-          IO::template stv_stream<(QPL < 4 ? QPL : 4)>(yb + loff + q * kB, ys + q);
+        for (int q = 0; q < QPL; q += (QPL < 16 / kB ? QPL : 16 / kB))   // 16-byte streaming stores
+          IO::template stv_stream<(QPL < 16 / kB ? QPL : 16 / kB)>(yb + loff + q * kB, ys + q);
       } else {
 #pragma unroll
         for (int q = 0; q < QPL; ++q)

@@ -133,7 +133,19 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lq = lane >> 4;
-  const int pslice = blockIdx.x, hh = blockIdx.y, b = blockIdx.z;
+  // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Renumber
+  // them so that XCD k runs a contiguous range of (slice, head, batch): the heads of one
+  // batch item that share a group's B and C chunks then read them from the same few L2s
+  // (measured: HBM reads 2.3x -> 1.1x the algorithmic bytes on 80 heads of 64, 128 states).
+  int pslice, hh, b;
+  {
+    const int nx = gridDim.x, ny = gridDim.y, total = nx * ny * gridDim.z;
+    int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    if (total % 8 == 0) id = (id % 8) * (total / 8) + id / 8;
+    pslice = id % nx;
+    hh = (id / nx) % ny;
+    b = id / (nx * ny);
+  }
   const int64_t L = p.L;
   const int H = p.H, P = p.P, G = p.G;
   const int g = hh / p.heads_per_group;
@@ -351,7 +363,9 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
         }
         if (t < nval) {
           const u32x2 o = {pack_bf(yv[0], yv[1]), pack_bf(yv[2], yv[3])};
-          __builtin_nontemporal_store(o, (u32x2*)(gY + ((int64_t)b * L + t0 + t) * rowX + colX + 16 * j + 4 * lq));
+          // plain stores: the L2 merges the 32-byte pieces of a line before writing it back
+          // (streaming stores wrote 1.4x the bytes of y)
+          *(u32x2*)(gY + ((int64_t)b * L + t0 + t) * rowX + colX + 16 * j + 4 * lq) = o;
         }
       }
     }
