@@ -251,7 +251,8 @@ def bench_decode(args, case, dev):
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    launch_ms = sum(per_launch) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     abytes = decode_bytes(case)
     achieved = abytes / (launch_ms * 1e-3) / 1e9
@@ -266,7 +267,8 @@ def bench_decode(args, case, dev):
                    "headdim": case.headdim, "ngroups": case.ngroups},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(args.workload),
-                     "kernel_ms": launch_ms, "algorithmic_bytes_per_launch": abytes},
+                     "kernel_ms": launch_ms, "kernel_ms_median": per_launch[len(per_launch) // 2],
+                     "kernel_ms_min": per_launch[0], "algorithmic_bytes_per_launch": abytes},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(case, args.cpu_budget)
@@ -361,7 +363,8 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    launch_ms = sum(per_launch) / args.steps
 
     ms_per_step = wall * 1e3 / args.steps
     elements = case.elements
@@ -393,7 +396,8 @@ def main():
                    "conv_width": args.conv, "plan": plan},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel_ms": launch_ms, "algorithmic_ops_per_launch": slots,
+                     "kernel_ms": launch_ms, "kernel_ms_median": per_launch[len(per_launch) // 2],
+                     "kernel_ms_min": per_launch[0], "algorithmic_ops_per_launch": slots,
                      "op": "fp32 VALU lane-issue slot (transcendental = 4)"},
         "hbm": {"algorithmic_bytes_per_launch": abytes, "achieved_GBs": hbm_gbs, "peak_GBs": HBM_PEAK_GBS,
                 "frac": hbm_gbs / HBM_PEAK_GBS},
