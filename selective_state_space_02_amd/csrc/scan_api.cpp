@@ -124,7 +124,8 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
   const char* ssd_env = std::getenv("SSM_SCAN_SSD");
   const bool ssd_ok = !(ssd_env && *ssd_env == '0');
   if (ssd_ok && d->layout == SSM_LAYOUT_BLHP && d->io_dtype == SSM_BF16 && (N == 32 || N == 64 || N == 128) &&
-      d->headdim % 16 == 0 && d->nheads <= 65535) {
+      d->headdim % 16 == 0 && d->nheads <= 65535 &&
+      64 * std::max<int64_t>(d->dim, d->ngroups * N) < ((int64_t)1 << 31)) {   // 32-bit offsets within a chunk
     p.kernel = 2;
     // positions per workgroup: 32 (two workgroups per CU), 16 when the head size needs it;
     // SSM_SSD_PS=16 forces 16 (tests, tuning)

@@ -206,30 +206,46 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   u32x4 pB[NBI], pC[NK], pU = {0u, 0u, 0u, 0u};
   u32x2 pUo[PT], pZo[PT];
   float pDelta;
-  auto prefetch = [&](int64_t tc) {
-    const int nv = (int)min((int64_t)Q, L - tc);
-    const uint16_t* const bB = gB + ((int64_t)b * L + tc) * rowBC + (int64_t)g * N;
+  // per-lane element offsets of a chunk's loads from its first step, for full chunks and
+  // for the last one (its steps past the end load its last valid step: in bounds, masked
+  // later); only a uniform chunk base is computed per chunk
+  struct Offs {
+    uint32_t B[NBI], C, X, XZ, dt;
+  };
+  auto offsets = [&](int nv) {
+    Offs o;
 #pragma unroll
     for (int k = 0; k < NBI; ++k) {
       const int it = tid + 256 * k, s = min(it / (N / 8), nv - 1), nb = (it % (N / 8)) * 8;
-      pB[k] = *(const u32x4*)(bB + s * rowBC + nb);
+      o.B[k] = (uint32_t)(s * rowBC + nb);
     }
     const int tC = min(16 * w + l16, nv - 1);
-    const uint16_t* const bC = gC + ((int64_t)b * L + tc + tC) * rowBC + (int64_t)g * N + 8 * lq;
+    o.C = (uint32_t)(tC * rowBC + 8 * lq);
+    o.X = (uint32_t)(min(tid / (PS / 8), nv - 1) * rowX + (tid % (PS / 8)) * 8);
+    o.XZ = (uint32_t)(tC * rowX + 4 * lq);
+    o.dt = (uint32_t)(min(lane, nv - 1) * H);
+    return o;
+  };
+  const Offs ofull = offsets(Q), olast = offsets((int)(L - last_chunk));
+  auto prefetch = [&](int64_t tc) {
+    const bool last = tc == last_chunk;
+    const int64_t row0 = (int64_t)b * L + tc;    // uniform
+    const uint16_t* const bB = gB + row0 * rowBC + (int64_t)g * N;
+#pragma unroll
+    for (int k = 0; k < NBI; ++k) pB[k] = *(const u32x4*)(bB + (last ? olast.B[k] : ofull.B[k]));
+    const uint16_t* const bC = gC + row0 * rowBC + (int64_t)g * N + (last ? olast.C : ofull.C);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) pC[kk] = *(const u32x4*)(bC + 32 * kk);
-    const uint16_t* const bX = gU + ((int64_t)b * L + tc) * rowX + colX;
-    if (tid < NUI) {
-      const int s = min(tid / (PS / 8), nv - 1), qb = (tid % (PS / 8)) * 8;
-      pU = *(const u32x4*)(bX + s * rowX + qb);
-    }
-    const uint16_t* const bZ = gZ + ((int64_t)b * L + tc) * rowX + colX;
+    const uint16_t* const bX = gU + row0 * rowX + colX;
+    if (tid < NUI) pU = *(const u32x4*)(bX + (last ? olast.X : ofull.X));
+    const uint32_t oxz = last ? olast.XZ : ofull.XZ;
+    const uint16_t* const bZ = gZ + row0 * rowX + colX;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      pUo[j] = *(const u32x2*)(bX + tC * rowX + 16 * j + 4 * lq);
-      pZo[j] = *(const u32x2*)(bZ + tC * rowX + 16 * j + 4 * lq);
+      pUo[j] = *(const u32x2*)(bX + oxz + 16 * j);
+      pZo[j] = *(const u32x2*)(bZ + oxz + 16 * j);
     }
-    pDelta = bf2f(gDt[((int64_t)b * L + tc + min(lane, nv - 1)) * H + hh]);
+    pDelta = bf2f(gDt[row0 * H + hh + (last ? olast.dt : ofull.dt)]);
   };
   prefetch(0);
 
@@ -314,11 +330,13 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
 #pragma unroll
           for (int kk = 0; kk < NK; ++kk)
             acc = mfma(ld8(&sB[(16 * i + l16) * BP + 32 * kk + 8 * lq]), __builtin_bit_cast(bf16x8, cC[kk]), acc);
+          // the decay of every lane, then a select: masked lanes (s > t) may hold inf, never used
+          const f32x4 cs = *(const f32x4*)&sCum[w][16 * i + 4 * lq];
           float m[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int s = 16 * i + 4 * lq + r;
-            m[r] = s <= t ? acc[r] * __builtin_amdgcn_exp2f(cum_t - sCum[w][s]) : 0.0f;
+            const float e = __builtin_amdgcn_exp2f(cum_t - cs[r]);
+            m[r] = 16 * i + 4 * lq + r <= t ? acc[r] * e : 0.0f;
           }
           split2(m[0], m[1], h0, l0);
           split2(m[2], m[3], h1, l1);
