@@ -151,18 +151,18 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
     p.bc_bytes = (size_t)d->batch * (size_t)d->ngroups * (size_t)p.nblk * (size_t)p.TB * 2 * (size_t)p.Npad *
                  sizeof(float);
     p.bc_bytes = (p.bc_bytes + 255) & ~(size_t)255;
-    // 16 states: an 80-channel launch (one workgroup per CU per segment, the same work on
-    // every SIMD) when its busiest SIMD has less to do than the plain launch's, over the
-    // main pass and (with time segments) the aggregate pass, which costs about 0.7 of a
-    // main pass per step.  A workgroup costs about 2.6 plain waves of work per SIMD.  The
-    // 80-channel launch picks its own segment count.  SSM_SCAN_MIXED=0/1 forces the choice
-    // (tests, tuning).  The 80-channel launch is the mixed one with 4 and 16 lanes per
-    // channel (independent waves, two per SIMD); SSM_SCAN_MIXED4=0 gives 8 and 16 lanes per
-    // channel (three waves per SIMD), SSM_SCAN_SPLIT=4 or 2 the split one (states over
-    // waves, 4 or 2 per wave, B/C in scalar registers, two workgroup barriers per block,
-    // one segment only; its tiles take twice the workspace).  Both measured slower on
-    // MI355X: the first spends more instructions and LDS traffic per element, the second
-    // stalls at its barriers.
+    // 16 states: a two-kind launch (one workgroup per CU per segment, the same channels on
+    // every SIMD) when its busiest SIMD has less to do than the plain launch's, over the main
+    // pass and (with time segments) the aggregate pass, which costs about 0.7 of a main pass
+    // per step.  Two workgroup sizes: 80 channels (4 lanes x 4 states, and 16 lanes x 1
+    // state; about 2.6 plain waves of work per SIMD) and 48 channels (8 lanes x 2 states,
+    // and 16 x 1; about 1.9).  Each picks its own segment count.  SSM_SCAN_MIXED=0 forces
+    // the plain launch, 1 the 80-channel one, 48 the 48-channel one (tests, tuning).  For
+    // 80 channels SSM_SCAN_MIXED4=0 gives 8 and 16 lanes per channel (three waves per SIMD),
+    // SSM_SCAN_SPLIT=4 or 2 the split launch (states over waves, 4 or 2 per wave, B/C in
+    // scalar registers, two workgroup barriers per block, one segment only; its tiles take
+    // twice the workspace).  Both measured slower on MI355X: the first spends more
+    // instructions and LDS traffic per element, the second stalls at its barriers.
     if (allow_mixed && p.Npad == 16) {
       const char* senv = std::getenv("SSM_SCAN_SPLIT");
       const bool split = senv && (*senv == '2' || *senv == '4');
@@ -176,38 +176,47 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
         const double agg = ns > 1 ? (double)((units * (ns - 1) + slots - 1) / slots) : 0.0;
         return unit_cost * (main + 0.7 * agg) * (double)len;
       };
-      const int64_t mixed_blocks = (rows_per_group + 79) / 80;
-      const int64_t wgs = mixed_blocks * groups_or_heads * d->batch;
+      struct Cand {
+        int64_t blocks, nseg;
+        double cost;
+      };
+      auto candidate = [&](int64_t rows, double unit_cost, bool search) {
+        Cand c;
+        c.blocks = (rows_per_group + rows - 1) / rows;
+        const int64_t wgs = c.blocks * groups_or_heads * d->batch;
+        c.nseg = seg_forced ? p.nseg : 1;
+        c.cost = pass_cost(wgs, kCUs, c.nseg, unit_cost);
+        if (!seg_forced && search) {
+          const int64_t max_seg = std::min<int64_t>(65535, (L + 255) / 256);
+          for (int64_t ns = 2; ns <= std::min<int64_t>(max_seg, 64); ++ns) {
+            const double cc = pass_cost(wgs, kCUs, ns, unit_cost);
+            if (cc < c.cost) { c.cost = cc; c.nseg = ns; }
+          }
+        }
+        return c;
+      };
       const int64_t waves = (int64_t)p.blocks_per_group * groups_or_heads * d->batch;
       const double cost_plain = pass_cost(waves, 4 * kCUs, p.nseg, 1.0);
-      int64_t best_nseg = 1;
-      double cost_mixed = pass_cost(wgs, kCUs, 1, 2.6);
-      if (seg_forced) {
-        best_nseg = p.nseg;
-        cost_mixed = pass_cost(wgs, kCUs, best_nseg, 2.6);
-      } else if (!split) {
-        const int64_t max_seg = std::min<int64_t>(65535, (L + 255) / 256);
-        for (int64_t ns = 2; ns <= std::min<int64_t>(max_seg, 64); ++ns) {
-          const double c = pass_cost(wgs, kCUs, ns, 2.6);
-          if (c < cost_mixed) { cost_mixed = c; best_nseg = ns; }
-        }
-      }
-      bool mixed = cost_mixed < cost_plain;
+      const Cand c80 = candidate(80, 2.6, !split), c48 = candidate(48, 1.9, true);
+      int rows = 0;   // 0: the plain launch
+      if (c80.cost < cost_plain) rows = 80;
+      if (c48.cost < std::min(cost_plain, c80.cost)) rows = 48;
       const char* env = std::getenv("SSM_SCAN_MIXED");
-      if (env && *env) mixed = *env != '0';
-      if (split && best_nseg != 1) mixed = false;   // the split launch runs one segment
-      if (mixed && groups_or_heads * mixed_blocks <= 0x7fffffff) {
+      if (env && *env) rows = *env == '0' ? 0 : std::atoi(env) == 48 ? 48 : 80;
+      if (split && rows == 80 && c80.nseg != 1) rows = 0;   // the split launch runs one segment
+      const Cand& c = rows == 48 ? c48 : c80;
+      if (rows && groups_or_heads * c.blocks <= 0x7fffffff) {
         const char* m4env = std::getenv("SSM_SCAN_MIXED4");
         const bool mixed4 = !(m4env && *m4env == '0');
-        p.kernel = split ? 4 : mixed4 ? 5 : 3;
-        p.ps = split ? *senv - '0' : 0;   // split launch: states per state wave
+        p.kernel = rows == 48 ? 6 : split ? 4 : mixed4 ? 5 : 3;
+        p.ps = p.kernel == 4 ? *senv - '0' : 0;   // split launch: states per state wave
         if (p.kernel == 5) p.vec_ok = p.vec_ok && d->seqlen % 8 == 0;   // 8-step vectors
         if (p.kernel == 4 && p.ps == 4) p.vec_ok = p.vec_ok && d->seqlen % 8 == 0;   // 8-step vectors
-        p.blocks_per_group = (int)mixed_blocks;
-        p.grid_rows = (int)(groups_or_heads * mixed_blocks);
+        p.blocks_per_group = (int)c.blocks;
+        p.grid_rows = (int)(groups_or_heads * c.blocks);
         if (p.kernel == 4) p.bc_bytes *= 2;
-        if (best_nseg != p.nseg) {   // the 80-channel launch's own segment count
-          int64_t len = round_up((L + best_nseg - 1) / best_nseg, p.TB);
+        if (c.nseg != p.nseg) {   // the two-kind launch's own segment count
+          int64_t len = round_up((L + c.nseg - 1) / c.nseg, p.TB);
           p.seg_len = len;
           p.nseg = (int)((L + len - 1) / len);
           p.seg_bytes = p.nseg > 1 ? (size_t)2 * (size_t)(p.nseg - 1) * (size_t)d->batch * (size_t)p.Npad *
@@ -261,7 +270,8 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
     std::snprintf(buf, buf_len,
                   "kernel=%s layout=%s io=%s disc=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d "
                   "ws=%zu%s",
-                  p.kernel == 5   ? "rowgroup_mixed4"
+                  p.kernel == 6   ? "rowgroup_mixed48"
+                  : p.kernel == 5 ? "rowgroup_mixed4"
                   : p.kernel == 4 ? "rowgroup_split"
                   : p.kernel == 3 ? "rowgroup_mixed"
                   : p.kernel == 2 ? "ssd"

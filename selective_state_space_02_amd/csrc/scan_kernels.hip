@@ -1064,24 +1064,29 @@ __global__ void __launch_bounds__(rg::MIX_WAVES * 64) rowgroup_mixed_kernel(KPar
   }
 }
 
-// mixed launch with 4 lanes per channel (16 states): waves 0..3 take 16 channels each with
-// 4 lanes of 4 states per channel, waves 4..7 take 4 channels each with 16 lanes per channel;
-// 80 channels per workgroup, waves w and w+4 share a SIMD.  Two waves per SIMD, but per
-// element a quarter less non-recurrence work and LDS traffic than 8 lanes per channel.
-template <typename IO, int MODE, bool VECOK, int SPF, int HZF>
-__global__ void __launch_bounds__(8 * 64) rowgroup_mixed4_kernel(KParams p) {
+// Two-kind launches (16 states), one workgroup per CU: waves 0..3 take 64/LPRA channels each
+// with LPRA lanes of 16/LPRA states per channel, waves 4..7 take 4 channels each with 16
+// lanes per channel; waves w and w+4 share a SIMD, so every SIMD holds the same channels.
+// LPRA = 4: 80 channels per workgroup (per element a quarter less non-recurrence work and
+// LDS traffic than 8 lanes per channel); LPRA = 8: 48 channels, for layers whose channel
+// count fills the CUs with 48 but not with 80.
+template <int LPRA>
+constexpr int pair_rows() { return 4 * (64 / LPRA) + 16; }
+
+template <typename IO, int LPRA, int MODE, bool VECOK, int SPF, int HZF>
+__global__ void __launch_bounds__(8 * 64) rowgroup_pair_kernel(KParams p) {
   using namespace rg;
   __shared__ __attribute__((aligned(16))) float s_tile[8][TILE];
   __shared__ __attribute__((aligned(16))) float s_bc[8][bc_tile<16>()];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.x / p.blocks_per_group;
-  const int rbase = (blockIdx.x % p.blocks_per_group) * MIX_ROWS;
+  const int rbase = (blockIdx.x % p.blocks_per_group) * pair_rows<LPRA>();
   if (wv < 4) {
-    const int r0 = rbase + 16 * wv;
+    const int r0 = rbase + (64 / LPRA) * wv;
     if (r0 >= p.rows_per_group) return;                      // no barriers: idle waves may leave
-    rowgroup_wave<IO, 4, 4, MODE, VECOK, false, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
+    rowgroup_wave<IO, LPRA, 16 / LPRA, MODE, VECOK, false, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
   } else {
-    const int r0 = rbase + 64 + 4 * (wv - 4);
+    const int r0 = rbase + 4 * (64 / LPRA) + 4 * (wv - 4);
     if (r0 >= p.rows_per_group) return;
     rowgroup_wave<IO, 16, 1, MODE, VECOK, false, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
   }
@@ -1440,36 +1445,43 @@ int launch_rowgroup_split(const KParams& kp, hipStream_t st) {
   return (int)hipGetLastError();
 }
 
-template <typename IO, bool VECOK, int SPF, int HZF>
-int launch_rowgroup_mixed4_f(const KParams& kp, hipStream_t st) {
+template <typename IO, int LPRA, bool VECOK, int SPF, int HZF>
+int launch_rowgroup_pair_f(const KParams& kp, hipStream_t st) {
   hipLaunchKernelGGL((bc_tile_kernel<IO, 16>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   const int gx = kp.blocks_per_group * kp.G;
   if (kp.nseg > 1) {   // aggregates of the segments before the last, then the main pass folds them
-    hipLaunchKernelGGL((rowgroup_mixed4_kernel<IO, 1, VECOK, SPF, HZF>), dim3(gx, kp.batch, kp.nseg - 1),
+    hipLaunchKernelGGL((rowgroup_pair_kernel<IO, LPRA, 1, VECOK, SPF, HZF>), dim3(gx, kp.batch, kp.nseg - 1),
                        dim3(8 * 64), 0, st, kp);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
-  hipLaunchKernelGGL((rowgroup_mixed4_kernel<IO, 0, VECOK, SPF, HZF>), dim3(gx, kp.batch, kp.nseg), dim3(8 * 64), 0,
-                     st, kp);
+  hipLaunchKernelGGL((rowgroup_pair_kernel<IO, LPRA, 0, VECOK, SPF, HZF>), dim3(gx, kp.batch, kp.nseg), dim3(8 * 64),
+                     0, st, kp);
   return (int)hipGetLastError();
 }
 
-template <typename IO, bool VECOK>
-int launch_rowgroup_mixed4(const KParams& kp, hipStream_t st) {
+// softplus and the gate as compile-time flags
+template <typename IO, int LPRA, bool VECOK>
+int launch_rowgroup_pair(const KParams& kp, hipStream_t st) {
   if (kp.softplus) {
-    return kp.has_z ? launch_rowgroup_mixed4_f<IO, VECOK, 1, 1>(kp, st) : launch_rowgroup_mixed4_f<IO, VECOK, 1, 0>(kp, st);
+    return kp.has_z ? launch_rowgroup_pair_f<IO, LPRA, VECOK, 1, 1>(kp, st)
+                    : launch_rowgroup_pair_f<IO, LPRA, VECOK, 1, 0>(kp, st);
   }
-  return kp.has_z ? launch_rowgroup_mixed4_f<IO, VECOK, 0, 1>(kp, st) : launch_rowgroup_mixed4_f<IO, VECOK, 0, 0>(kp, st);
+  return kp.has_z ? launch_rowgroup_pair_f<IO, LPRA, VECOK, 0, 1>(kp, st)
+                  : launch_rowgroup_pair_f<IO, LPRA, VECOK, 0, 0>(kp, st);
 }
 
 template <int LAYOUT, typename IO>
 int launch_io(const Plan& pl, const KParams& kp, hipStream_t st) {
-  if (LAYOUT == 0 && pl.kernel == 5) {
-    if (kp.L % 8 == 0) return launch_rowgroup_mixed4<IO, true>(kp, st);
-    return launch_rowgroup_mixed4<IO, false>(kp, st);
+  if (LAYOUT == 0 && pl.kernel == 5) {   // 8-step vectors per lane
+    if (kp.L % 8 == 0) return launch_rowgroup_pair<IO, 4, true>(kp, st);
+    return launch_rowgroup_pair<IO, 4, false>(kp, st);
+  }
+  if (LAYOUT == 0 && pl.kernel == 6) {   // 4-step vectors per lane
+    if (kp.L % 4 == 0) return launch_rowgroup_pair<IO, 8, true>(kp, st);
+    return launch_rowgroup_pair<IO, 8, false>(kp, st);
   }
   if (LAYOUT == 0 && pl.kernel == 4) {
     if (pl.ps == 2) {

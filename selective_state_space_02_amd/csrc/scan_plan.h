@@ -19,7 +19,9 @@ struct Plan {
   int kernel = 0;            // 0: workgroup kernel (64 rows, states over waves); 1: row-group kernel;
                              // 2: chunked multi-head kernel on MFMA (ssd_kernels.hip);
                              // 3: row-group kernel, mixed launch (16 states, 80 channels per workgroup);
-                             // 4: row-group kernel, split launch (16 states, 80 channels per workgroup)
+                             // 4: row-group kernel, split launch (16 states, 80 channels per workgroup);
+                             // 5 / 6: row-group kernel, two-kind launch (16 states, 80 / 48 channels
+                             // per workgroup)
   int ps = 0;                // kernel 2: positions per workgroup
   int disc = 0;              // SSM_DISC_DELTA_B or SSM_DISC_ZOH
   int layout = 0, io = 0;

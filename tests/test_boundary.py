@@ -130,8 +130,8 @@ def test_workspace_size_and_plan():
     assert "seg_len=2048" in scan.describe(d)
     txt = scan.describe(d)
     assert "kernel=rowgroup_mixed4" in txt and "layout=bdl" in txt and "grid=(64,4,1)" in txt
-    d2 = dims(batch=8, seqlen=2048, dim=1536, dstate=16)              # 1536 waves: the plain launch
-    assert "kernel=rowgroup " in scan.describe(d2) and "grid=(48,8,1)" in scan.describe(d2)
+    d2 = dims(batch=8, seqlen=2048, dim=1536, dstate=16)              # 256 workgroups of 48 channels
+    assert "kernel=rowgroup_mixed48" in scan.describe(d2) and "grid=(32,8,1)" in scan.describe(d2)
     d32 = dims(batch=4, seqlen=2048, dim=5120, dstate=32)             # 32 states: plain
     assert "kernel=rowgroup " in scan.describe(d32)
     d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # 32 workgroups: 8 time segments
@@ -235,12 +235,14 @@ def test_ssd_override_env(monkeypatch):
 
 
 def test_mixed_launch_override_env(monkeypatch):
-    """SSM_SCAN_MIXED forces the 16-state launch shape; SSM_SCAN_MIXED4=0 and SSM_SCAN_SPLIT=4/2 select
-    the other 80-channel launches."""
+    """SSM_SCAN_MIXED forces the 16-state launch shape (0 plain, 1 80 channels, 48 channels);
+    SSM_SCAN_MIXED4=0 and SSM_SCAN_SPLIT=4/2 select the other 80-channel launches."""
     d = dims(batch=4, seqlen=2048, dim=5120, dstate=16)
     ws = scan.workspace_size(d)
     monkeypatch.setenv("SSM_SCAN_MIXED", "0")
     assert "kernel=rowgroup " in scan.describe(d) and scan.workspace_size(d) == ws
+    monkeypatch.setenv("SSM_SCAN_MIXED", "48")
+    assert "kernel=rowgroup_mixed48" in scan.describe(d) and "grid=(107,4,1)" in scan.describe(d)
     monkeypatch.setenv("SSM_SCAN_MIXED", "1")
     d2 = dims(batch=8, seqlen=2048, dim=1536, dstate=16)
     assert "kernel=rowgroup_mixed4" in scan.describe(d2) and "grid=(20,8,1)" in scan.describe(d2)

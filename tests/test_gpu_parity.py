@@ -206,7 +206,8 @@ def test_continuation_matches_single_call():
 LAUNCH16 = {"split4": ({"SSM_SCAN_SPLIT": "4"}, "kernel=rowgroup_split", "states_per_wave=4"),
             "split2": ({"SSM_SCAN_SPLIT": "2"}, "kernel=rowgroup_split", "states_per_wave=2"),
             "mixed4": ({}, "kernel=rowgroup_mixed4", ""),
-            "mixed": ({"SSM_SCAN_MIXED4": "0"}, "kernel=rowgroup_mixed ", "")}
+            "mixed": ({"SSM_SCAN_MIXED4": "0"}, "kernel=rowgroup_mixed ", ""),
+            "mixed48": ({"SSM_SCAN_MIXED": "48"}, "kernel=rowgroup_mixed48", "")}
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -230,7 +231,7 @@ def test_mixed_launch(io, D, L, G, launch, monkeypatch):
     check_case(c)
 
 
-@pytest.mark.parametrize("launch", ["mixed4", "mixed"])
+@pytest.mark.parametrize("launch", ["mixed4", "mixed", "mixed48"])
 @pytest.mark.parametrize("L,nseg", [(1000, "3"), (97, "3"), (4100, "5")])
 def test_mixed_launch_segments(L, nseg, launch, monkeypatch):
     """The 80-channel launches over time segments: an aggregate pass per segment before the
@@ -263,8 +264,8 @@ def test_mixed_launch_options(opts, launch, monkeypatch):
 
 
 def test_mixed_and_plain_agree():
-    """The three launches of the 16-state layer: the same recurrence per state; only the order
-    of the readout sum over states differs."""
+    """The launches of the 16-state layer: the same recurrence per state; only the order of the
+    readout sum over states differs."""
     c = make_case("mix_vs_plain", layout="bdl", io_dtype="bf16", batch=2, seqlen=512, dim=320, dstate=16,
                   seed=12, has_h0=True, A_kind="lognormal")
     saved = {k: os.environ.get(k) for k in ("SSM_SCAN_MIXED", "SSM_SCAN_SPLIT", "SSM_SCAN_MIXED4")}
@@ -279,6 +280,8 @@ def test_mixed_and_plain_agree():
         y1, h1 = gpu_run(c)
         os.environ["SSM_SCAN_MIXED4"] = "1"
         y4, h4 = gpu_run(c)
+        os.environ["SSM_SCAN_MIXED"] = "48"
+        y5, h5 = gpu_run(c)
         os.environ["SSM_SCAN_MIXED"] = "0"
         y0, h0 = gpu_run(c)
     finally:
@@ -287,6 +290,6 @@ def test_mixed_and_plain_agree():
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
-    for y, h in ((y1, h1), (y2, h2), (y3, h3), (y4, h4)):
+    for y, h in ((y1, h1), (y2, h2), (y3, h3), (y4, h4), (y5, h5)):
         torch.testing.assert_close(y.float(), y0.float(), rtol=1e-2, atol=1e-2)
         torch.testing.assert_close(h, h0, rtol=1e-5, atol=1e-5)
