@@ -86,9 +86,10 @@ def kernel_source_hash(workload: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they match this kernel."""
-    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
+def load_traffic(workload: str, variant: str = ""):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they match this kernel.
+    variant: "" or the path's options ("_zoh", "_conv4", "_zoh_conv4")."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}{variant}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -374,7 +375,8 @@ def main():
     achieved = slots / (launch_ms * 1e-3) / 1e12
     peak = VALU_SLOT_PEAK / 1e12
     abytes = algorithmic_bytes(case) + (case.dim * (args.conv + 1) * 4 if args.conv else 0)
-    traffic = load_traffic(args.workload) if not (args.conv or args.discretization != "delta_b") else None
+    variant = ("_zoh" if args.discretization == "zoh" else "") + (f"_conv{args.conv}" if args.conv else "")
+    traffic = load_traffic(args.workload, variant)
     hbm_gbs = abytes / (launch_ms * 1e-3) / 1e9
 
     line = {
