@@ -63,7 +63,7 @@ bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u); }
 
 }  // namespace
 
-int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
+int make_plan(const ssm_dims_t* d, Plan* pl, bool conv) {
   if (!d || !pl) return SSM_ERR_NULL_ARG;
   if (d->layout != SSM_LAYOUT_BDL && d->layout != SSM_LAYOUT_BLHP) return SSM_ERR_UNSUPPORTED;
   if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
@@ -163,9 +163,9 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool allow_mixed) {
     // scalar registers, two workgroup barriers per block, one segment only; its tiles take
     // twice the workspace).  Both measured slower on MI355X: the first spends more
     // instructions and LDS traffic per element, the second stalls at its barriers.
-    if (allow_mixed && p.Npad == 16) {
+    if (p.Npad == 16) {
       const char* senv = std::getenv("SSM_SCAN_SPLIT");
-      const bool split = senv && (*senv == '2' || *senv == '4');
+      const bool split = !conv && senv && (*senv == '2' || *senv == '4');   // no input stage in the split launch
       const char* seg_env = std::getenv("SSM_SCAN_SEGMENTS");
       const bool seg_forced = seg_env && *seg_env;
       const int64_t L = d->seqlen;
@@ -291,7 +291,7 @@ static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, 
   ssm::g_hip_msg[0] = 0;
   if (!u || !delta || !A || !B || !C || !y || !dims) return SSM_ERR_NULL_ARG;
   ssm::Plan pl;
-  int rc = ssm::make_plan(dims, &pl, conv == nullptr);   // the fused input stage runs in the plain launch
+  int rc = ssm::make_plan(dims, &pl, conv != nullptr);
   if (rc != SSM_OK) return rc;
   const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, y, h_last};
   for (const void* q : ptrs)
@@ -299,7 +299,8 @@ static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, 
   if (conv) {
     if (!conv->weight) return SSM_ERR_NULL_ARG;
     if (conv->width < 1 || conv->width > 4 || conv->reserved != 0) return SSM_ERR_UNSUPPORTED;
-    if (pl.kernel != 1) return SSM_ERR_UNSUPPORTED;   // the fused stage lives in the per-channel kernel
+    // the fused stage lives in the per-channel (row-group) kernels
+    if (pl.kernel != 1 && pl.kernel != 3 && pl.kernel != 5 && pl.kernel != 6) return SSM_ERR_UNSUPPORTED;
     const void* cps[] = {conv->weight, conv->bias, conv->state_in, conv->state_out};
     for (const void* q : cps)
       if (ssm::misaligned(q)) return SSM_ERR_ALIGN;

@@ -685,7 +685,6 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
   constexpr int NCK = QPL * kB > 16 ? QPL * kB / 16 : 1;      // 16-byte chunks of QPL steps
   using RawQ = typename RawT<QPL * kB / NCK>::T;             // one chunk of one tensor
   static_assert(QPL == 8 || QPL == 4 || QPL == 2, "4, 8 or 16 lanes per channel");
-  static_assert(!CONV || QPL == 4, "the input stage needs 4 steps per lane");
 
   const int lane = threadIdx.x & 63;
   const int row = lane / LPR, k = lane % LPR;
@@ -744,7 +743,7 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
   // ---- optional input stage: causal depthwise convolution (width K <= 4) + SiLU
   // The filter is held right-aligned in 4 taps (leading taps 0), so step t reads the
   // raw inputs t-3..t.  carry[] holds the 3 raw inputs before the current block; only
-  // the row's last lane (the row's last 4 steps) carries them to the next block.
+  // the row's last lane (the row's last QPL steps) carries them to the next block.
   float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f, carry[3] = {0.0f, 0.0f, 0.0f};
   if (CONV) {
     const int K = p.conv_k;
@@ -769,19 +768,27 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
                        const float (&zz)[QPL]) {
     float uu[QPL];
     if constexpr (CONV) {
-      // raw inputs of the 3 steps before this lane's first: lane k-1's last 3, or the carry
-      float xw[7];
+      // xw[j]: raw input at step QPL*k - 3 + j of the block.  The 3 before this lane's
+      // first step sit in the lanes to its left (register reg of lane k + lo), or, before
+      // the block, in the row's last lane's carry.
+      float xw[QPL + 3];
+      const int last = (lane & ~(LPR - 1)) + LPR - 1;
+      const float c0 = __shfl(carry[0], last), c1 = __shfl(carry[1], last), c2 = __shfl(carry[2], last);
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
-        const float from_left = __shfl(uin[1 + i], lane > 0 ? lane - 1 : 0);
-        const float from_carry = __shfl(carry[i], (lane & ~(LPR - 1)) + LPR - 1);
-        xw[i] = k == 0 ? from_carry : from_left;
-        carry[i] = uin[1 + i];
+        const int s_off = i - 3;                                  // step relative to the lane's first
+        const int lo = -((-s_off + QPL - 1) / QPL), reg = s_off - lo * QPL;
+        const float from_left = __shfl(uin[reg], lane + lo >= 0 ? lane + lo : 0);
+        const int cidx = QPL * k + s_off + 3;                     // < 3: before the block
+        const float from_carry = cidx == 0 ? c0 : cidx == 1 ? c1 : c2;
+        xw[i] = k + lo < 0 ? from_carry : from_left;
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xw[3 + q] = uin[q];
+      for (int q = 0; q < QPL; ++q) xw[3 + q] = uin[q];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int i = 0; i < 3; ++i) carry[i] = xw[QPL + i];         // this lane's last 3 steps
+#pragma unroll
+      for (int q = 0; q < QPL; ++q) {
         float c = cb;
 #pragma unroll
         for (int m = 0; m < 4; ++m) c = fmaf(cw[m], xw[q + m], c);
@@ -1045,7 +1052,7 @@ rowgroup_kernel(KParams p) {
 
 // mixed launch (16 states): waves 0..7 take 8 channels each with 8 lanes per channel,
 // waves 8..11 take 4 channels each with 16 lanes per channel; 80 channels per workgroup
-template <typename IO, int MODE, bool VECOK>
+template <typename IO, int MODE, bool VECOK, bool CONV>
 __global__ void __launch_bounds__(rg::MIX_WAVES * 64) rowgroup_mixed_kernel(KParams p) {
   using namespace rg;
   __shared__ __attribute__((aligned(16))) float s_tile[MIX_WAVES][TILE];
@@ -1056,11 +1063,11 @@ __global__ void __launch_bounds__(rg::MIX_WAVES * 64) rowgroup_mixed_kernel(KPar
   if (wv < 8) {
     const int r0 = rbase + 8 * wv;
     if (r0 >= p.rows_per_group) return;                      // no barriers: idle waves may leave
-    rowgroup_wave<IO, 8, 2, MODE, VECOK, false>(p, g, r0, s_tile[wv], s_bc[wv]);
+    rowgroup_wave<IO, 8, 2, MODE, VECOK, CONV>(p, g, r0, s_tile[wv], s_bc[wv]);
   } else {
     const int r0 = rbase + 64 + 4 * (wv - 8);
     if (r0 >= p.rows_per_group) return;
-    rowgroup_wave<IO, 16, 1, MODE, VECOK, false>(p, g, r0, s_tile[wv], s_bc[wv]);
+    rowgroup_wave<IO, 16, 1, MODE, VECOK, CONV>(p, g, r0, s_tile[wv], s_bc[wv]);
   }
 }
 
@@ -1073,7 +1080,7 @@ __global__ void __launch_bounds__(rg::MIX_WAVES * 64) rowgroup_mixed_kernel(KPar
 template <int LPRA>
 constexpr int pair_rows() { return 4 * (64 / LPRA) + 16; }
 
-template <typename IO, int LPRA, int MODE, bool VECOK, int SPF, int HZF>
+template <typename IO, int LPRA, int MODE, bool VECOK, int SPF, int HZF, bool CONV>
 __global__ void __launch_bounds__(8 * 64) rowgroup_pair_kernel(KParams p) {
   using namespace rg;
   __shared__ __attribute__((aligned(16))) float s_tile[8][TILE];
@@ -1084,11 +1091,11 @@ __global__ void __launch_bounds__(8 * 64) rowgroup_pair_kernel(KParams p) {
   if (wv < 4) {
     const int r0 = rbase + (64 / LPRA) * wv;
     if (r0 >= p.rows_per_group) return;                      // no barriers: idle waves may leave
-    rowgroup_wave<IO, LPRA, 16 / LPRA, MODE, VECOK, false, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
+    rowgroup_wave<IO, LPRA, 16 / LPRA, MODE, VECOK, CONV, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
   } else {
     const int r0 = rbase + 4 * (64 / LPRA) + 4 * (wv - 4);
     if (r0 >= p.rows_per_group) return;
-    rowgroup_wave<IO, 16, 1, MODE, VECOK, false, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
+    rowgroup_wave<IO, 16, 1, MODE, VECOK, CONV, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
   }
 }
 
@@ -1418,21 +1425,27 @@ int launch_rowgroup(const Plan& pl, const KParams& kp, hipStream_t st) {
   return launch_rowgroup_modes<IO, NS, false, false>(pl, kp, st);
 }
 
-template <typename IO, bool VECOK>
-int launch_rowgroup_mixed(const KParams& kp, hipStream_t st) {
+template <typename IO, bool VECOK, bool CONV>
+int launch_rowgroup_mixed_c(const KParams& kp, hipStream_t st) {
   hipLaunchKernelGGL((bc_tile_kernel<IO, 16>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   const int gx = kp.blocks_per_group * kp.G;
   if (kp.nseg > 1) {
-    hipLaunchKernelGGL((rowgroup_mixed_kernel<IO, 1, VECOK>), dim3(gx, kp.batch, kp.nseg - 1),
+    hipLaunchKernelGGL((rowgroup_mixed_kernel<IO, 1, VECOK, CONV>), dim3(gx, kp.batch, kp.nseg - 1),
                        dim3(rg::MIX_WAVES * 64), 0, st, kp);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
-  hipLaunchKernelGGL((rowgroup_mixed_kernel<IO, 0, VECOK>), dim3(gx, kp.batch, kp.nseg), dim3(rg::MIX_WAVES * 64), 0,
-                     st, kp);
+  hipLaunchKernelGGL((rowgroup_mixed_kernel<IO, 0, VECOK, CONV>), dim3(gx, kp.batch, kp.nseg),
+                     dim3(rg::MIX_WAVES * 64), 0, st, kp);
   return (int)hipGetLastError();
+}
+
+template <typename IO, bool VECOK>
+int launch_rowgroup_mixed(const KParams& kp, hipStream_t st) {
+  return kp.conv_k > 0 ? launch_rowgroup_mixed_c<IO, VECOK, true>(kp, st)
+                       : launch_rowgroup_mixed_c<IO, VECOK, false>(kp, st);
 }
 
 template <typename IO, bool VECOK, int NSW>
@@ -1445,32 +1458,33 @@ int launch_rowgroup_split(const KParams& kp, hipStream_t st) {
   return (int)hipGetLastError();
 }
 
-template <typename IO, int LPRA, bool VECOK, int SPF, int HZF>
+template <typename IO, int LPRA, bool VECOK, int SPF, int HZF, bool CONV>
 int launch_rowgroup_pair_f(const KParams& kp, hipStream_t st) {
   hipLaunchKernelGGL((bc_tile_kernel<IO, 16>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   const int gx = kp.blocks_per_group * kp.G;
   if (kp.nseg > 1) {   // aggregates of the segments before the last, then the main pass folds them
-    hipLaunchKernelGGL((rowgroup_pair_kernel<IO, LPRA, 1, VECOK, SPF, HZF>), dim3(gx, kp.batch, kp.nseg - 1),
+    hipLaunchKernelGGL((rowgroup_pair_kernel<IO, LPRA, 1, VECOK, SPF, HZF, CONV>), dim3(gx, kp.batch, kp.nseg - 1),
                        dim3(8 * 64), 0, st, kp);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
-  hipLaunchKernelGGL((rowgroup_pair_kernel<IO, LPRA, 0, VECOK, SPF, HZF>), dim3(gx, kp.batch, kp.nseg), dim3(8 * 64),
+  hipLaunchKernelGGL((rowgroup_pair_kernel<IO, LPRA, 0, VECOK, SPF, HZF, CONV>), dim3(gx, kp.batch, kp.nseg), dim3(8 * 64),
                      0, st, kp);
   return (int)hipGetLastError();
 }
 
-// softplus and the gate as compile-time flags
+// softplus and the gate as compile-time flags; with the fused input stage both stay run-time
 template <typename IO, int LPRA, bool VECOK>
 int launch_rowgroup_pair(const KParams& kp, hipStream_t st) {
+  if (kp.conv_k > 0) return launch_rowgroup_pair_f<IO, LPRA, VECOK, -1, -1, true>(kp, st);
   if (kp.softplus) {
-    return kp.has_z ? launch_rowgroup_pair_f<IO, LPRA, VECOK, 1, 1>(kp, st)
-                    : launch_rowgroup_pair_f<IO, LPRA, VECOK, 1, 0>(kp, st);
+    return kp.has_z ? launch_rowgroup_pair_f<IO, LPRA, VECOK, 1, 1, false>(kp, st)
+                    : launch_rowgroup_pair_f<IO, LPRA, VECOK, 1, 0, false>(kp, st);
   }
-  return kp.has_z ? launch_rowgroup_pair_f<IO, LPRA, VECOK, 0, 1>(kp, st)
-                  : launch_rowgroup_pair_f<IO, LPRA, VECOK, 0, 0>(kp, st);
+  return kp.has_z ? launch_rowgroup_pair_f<IO, LPRA, VECOK, 0, 1, false>(kp, st)
+                  : launch_rowgroup_pair_f<IO, LPRA, VECOK, 0, 0, false>(kp, st);
 }
 
 template <int LAYOUT, typename IO>

@@ -93,8 +93,8 @@ struct UParams {
 };
 
 // Validates dims (no HIP call) and fills the plan; returns SSM_OK or an error code.
-// allow_mixed = false keeps the plain row-group launch (the fused input stage needs it).
-int make_plan(const ssm_dims_t* d, Plan* plan, bool allow_mixed = true);
+// conv: the plan of a call with the fused input stage (every launch but the split one).
+int make_plan(const ssm_dims_t* d, Plan* plan, bool conv = false);
 
 // Enqueue the kernels of a validated plan.  Returns a hipError_t value (0 = success).
 // scan_kernels.hip is compiled once per discretization; launch_plan picks the build.

@@ -2,7 +2,9 @@
 through ssm_conv_scan_fwd, against the oracle's conv_scan.  Widths 1..4, ragged
 sequence lengths (element path), 16 and 32 states, forced time segments (the
 segment's first block reads the 3 raw inputs before it), a carried conv state in
-and out, the exact-hold discretization, and a two-call continuation.
+and out, the exact-hold discretization, a two-call continuation, and every
+16-state launch (2, 4, 8 or 16 steps per lane take their 3 earlier raw inputs
+from one or two lanes to the left, or from the carry of the previous block).
 Tolerances as for the scan: 1e-4 (float32) and 2e-2 (bfloat16) relative to 1 + |ref|.
 """
 import numpy as np
@@ -82,6 +84,35 @@ def test_conv_scan(name, kw, K, with_state, segs, disc, monkeypatch):
     print(f"[gpu] conv scan {name} K={K} state={with_state} segments={segs} disc={disc}", flush=True)
     y, h, cs = run(c, w, b, st, disc)
     y_ref, h_ref, cs_ref = ref(c, w, b, st, "zoh" if disc == "zoh" else "euler")
+    tol = TOL[c.io_dtype]
+    ey, eh = scaled_err(y, y_ref), scaled_err(h, h_ref)
+    print(f"[gpu]   max scaled err y {ey:.2e} h {eh:.2e}", flush=True)
+    assert ey <= tol and eh <= tol
+    np.testing.assert_array_equal(cs.double().cpu().numpy(), cs_ref)
+
+
+LAUNCHES = {"plain": {"SSM_SCAN_MIXED": "0"}, "mixed4": {"SSM_SCAN_MIXED": "1"},
+            "mixed": {"SSM_SCAN_MIXED": "1", "SSM_SCAN_MIXED4": "0"}, "mixed48": {"SSM_SCAN_MIXED": "48"}}
+LAUNCH_CASES = [
+    ("bf16-K4", dict(io_dtype="bf16", batch=2, seqlen=320, dim=136, dstate=16), 4, True, None),
+    ("f32-K3-ragged", dict(io_dtype="f32", batch=2, seqlen=97, dim=90, dstate=16), 3, True, None),
+    ("f32-K4-segments", dict(io_dtype="f32", batch=1, seqlen=1100, dim=100, dstate=13), 4, True, "3"),
+    ("bf16-K2-nostate", dict(io_dtype="bf16", batch=1, seqlen=200, dim=48, dstate=16), 2, False, None),
+]
+
+
+@pytest.mark.parametrize("launch", list(LAUNCHES))
+@pytest.mark.parametrize("name,kw,K,with_state,segs", LAUNCH_CASES, ids=[c[0] for c in LAUNCH_CASES])
+def test_conv_scan_launches(name, kw, K, with_state, segs, launch, monkeypatch):
+    for k, v in LAUNCHES[launch].items():
+        monkeypatch.setenv(k, v)
+    if segs:
+        monkeypatch.setenv("SSM_SCAN_SEGMENTS", segs)
+    c = make_case(name, layout="bdl", seed=53, has_h0=True, A_kind="lognormal", **kw)
+    w, b, st = conv_params(c.dim, K, c.batch, 54, with_state)
+    print(f"[gpu] conv scan {name} launch={launch} K={K} segments={segs}", flush=True)
+    y, h, cs = run(c, w, b, st)
+    y_ref, h_ref, cs_ref = ref(c, w, b, st)
     tol = TOL[c.io_dtype]
     ey, eh = scaled_err(y, y_ref), scaled_err(h, h_ref)
     print(f"[gpu]   max scaled err y {ey:.2e} h {eh:.2e}", flush=True)
