@@ -54,7 +54,7 @@ struct KParams {
   float* wsH;   // [seg][b][n][d] zero-start end state of each aggregated segment
   float* bct;   // row-group kernel: [b][g][block] B/C tiles in LDS order (bc_tile_kernel)
   float* bct2;  // split launch: the same tiles per state pair, [b][g][block][pair][t][B C B C]
-  const float* conv_w;     // optional input stage (row-group kernel): (dim, conv_k) filters
+  const float* conv_w;     // optional input stage (row-group kernels): (dim, conv_k) filters
   const float* conv_b;     // (dim) or NULL
   const float* conv_sin;   // (batch, dim, conv_k-1) raw inputs before t = 0, or NULL (zeros)
   float* conv_sout;        // (batch, dim, conv_k-1) last raw inputs, or NULL
@@ -63,7 +63,8 @@ struct KParams {
   int64_t L, seg_len;
   int batch, dim, N, Npad, H, P, G;
   int rows_per_group;    // BDL: dim / G;  BLHP: P
-  int blocks_per_group;  // row blocks per group / head (64 rows; 8 for the row-group kernel, 80 mixed)
+  int blocks_per_group;  // row blocks per group / head (64 rows; 8 for the row-group kernel; 80 or 48 for
+                         // the two-kind launches, 80 for the mixed and split ones)
   int heads_per_group;   // BLHP: H / G
   int softplus;
   int has_z;
