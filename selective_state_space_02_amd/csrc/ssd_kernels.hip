@@ -99,6 +99,19 @@ __device__ __forceinline__ bf16x8 ld8_tr(const uint16_t* base, int k0, int r0, i
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// The same with the 32 contraction rows taken as two halves of 16, in the row order of
+// two 16x16 MFMA results (rows 4 lq + r): lane (l16, lq) receives rows k0 + 4 lq .. +3
+// and k0 + 16 + 4 lq .. +3 of column r0 + l16.
+template <int RS>
+__device__ __forceinline__ bf16x8 ld8_tr_halves(const uint16_t* base, int k0, int r0, int l16, int lq) {
+  const uint16_t* p0 = base + (k0 + 4 * lq + (l16 >> 2)) * RS + r0 + 4 * (l16 & 3);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+  const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 16 * RS));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Q = 64 steps per chunk, N states (32, 64 or 128), PS positions per workgroup (16 or 32).
 // MFMA lane layout (16x16x32): A row = lane%16, k = 8*(lane/16)+i; B column = lane%16,
 // k = 8*(lane/16)+i; D column = lane%16, rows 4*(lane/16)+r.
@@ -111,7 +124,6 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   constexpr int BP = N == 32 ? 56 : N == 64 ? 72 : 152;   // sB [s][n]: read plainly and transposed
   constexpr int NP = N + 8;            // sH [p][n]: plain reads only
   constexpr int XP = PS == 16 ? 56 : 72;   // sX, sXW [s][hi p | lo p]: transposed reads
-  constexpr int MP = Q + 8;            // sM [t][s]
   static_assert(BP >= N && XP >= 2 * PS, "row strides");
   constexpr int NK = N / 32;           // 32-wide contraction steps over states
   constexpr int PT = PS / 16;          // 16-wide position tiles
@@ -125,7 +137,6 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sB[Q * BP];         // B [s][n]
   __shared__ __attribute__((aligned(16))) uint16_t sX[Q * XP];         // dt*u [s][hi p | lo p]
   __shared__ __attribute__((aligned(16))) uint16_t sXW[Q * XP];        // e^{cum_end - cum_s} dt*u, same
-  __shared__ __attribute__((aligned(16))) uint16_t sM[4][2][16 * MP];  // per wave: M^T of its 16 steps [t][s]
   __shared__ __attribute__((aligned(16))) uint16_t sH[2][PS * NP];     // state [p][n], hi / lo
   __shared__ float sCum[4][Q];                                         // per wave: cum (log2 units)
   __shared__ float sDt[4][Q];                                          // per wave: step sizes
@@ -318,11 +329,16 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
     const int ks = 32 * ((w + 2) / 2);   // contraction range over steps covering s <= 16w+15
     {
       // M^T = (B C^T) o decay for the step tiles i <= w of this wave's column tile (zeros
-      // for i > w inside the range ks), stored [t][s] with 8-byte writes (wave-private)
+      // for i > w inside the range ks), kept in registers as hi / lo bf16 pairs in the
+      // layout of the MFMA result (lane: step t, steps s = 16 i + 4 lq + r), which is the
+      // operand layout of the next product with its contraction rows taken in two halves
       const int t = 16 * w + l16;
       const float cum_t = sCum[w][t];
+      u32x2 mh[4], ml[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        mh[i] = (u32x2){0u, 0u};
+        ml[i] = (u32x2){0u, 0u};
         if (16 * i >= ks) continue;
         uint32_t h0 = 0, l0 = 0, h1 = 0, l1 = 0;
         if (i <= w) {
@@ -341,26 +357,24 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
           split2(m[0], m[1], h0, l0);
           split2(m[2], m[3], h1, l1);
         }
-        const int o = l16 * MP + 16 * i + 4 * lq;
-        *(u32x2*)&sM[w][0][o] = (u32x2){h0, h1};
-        *(u32x2*)&sM[w][1][o] = (u32x2){l0, l1};
+        mh[i] = (u32x2){h0, h1};
+        ml[i] = (u32x2){l0, l1};
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
       // Y^T = X^T M^T + H^T C^T per position tile; lane: step t, positions 16 j + 4 lq + r
       const float et = __builtin_amdgcn_exp2f(cum_t);
 #pragma unroll
       for (int j = 0; j < PT; ++j) {
         f32x4 yd = {0.f, 0.f, 0.f, 0.f}, yo = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < ks; kk += 32) {
-          const bf16x8 xa = ld8_tr<XP>(sX, kk, 16 * j, l16, lq);
-          const bf16x8 xl = ld8_tr<XP>(sX, kk, PS + 16 * j, l16, lq);
-          const bf16x8 mb = ld8(&sM[w][0][l16 * MP + kk + 8 * lq]);
-          const bf16x8 ml = ld8(&sM[w][1][l16 * MP + kk + 8 * lq]);
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {   // steps s in [32 kc, 32 kc + 32): M tiles 2 kc, 2 kc + 1
+          if (32 * kc >= ks) continue;     // uniform
+          const bf16x8 xa = ld8_tr_halves<XP>(sX, 32 * kc, 16 * j, l16, lq);
+          const bf16x8 xl = ld8_tr_halves<XP>(sX, 32 * kc, PS + 16 * j, l16, lq);
+          const bf16x8 mb = __builtin_bit_cast(bf16x8, (u32x4){mh[2 * kc][0], mh[2 * kc][1], mh[2 * kc + 1][0], mh[2 * kc + 1][1]});
+          const bf16x8 mlo = __builtin_bit_cast(bf16x8, (u32x4){ml[2 * kc][0], ml[2 * kc][1], ml[2 * kc + 1][0], ml[2 * kc + 1][1]});
           yd = mfma(xa, mb, yd);
-          yd = mfma(xa, ml, yd);
+          yd = mfma(xa, mlo, yd);
           yd = mfma(xl, mb, yd);
         }
 #pragma unroll
