@@ -156,7 +156,7 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool conv) {
     // pass and (with time segments) the aggregate pass, which costs about 0.7 of a main pass
     // per step.  Two workgroup sizes: 80 channels (4 lanes x 4 states, and 16 lanes x 1
     // state; about 2.6 plain waves of work per SIMD) and 48 channels (8 lanes x 2 states,
-    // and 16 x 1; about 1.9).  Each picks its own segment count.  SSM_SCAN_MIXED=0 forces
+    // and 16 x 1; about 1.9).  The 80-channel one picks its own segment count.  SSM_SCAN_MIXED=0 forces
     // the plain launch, 1 the 80-channel one, 48 the 48-channel one (tests, tuning).  For
     // 80 channels SSM_SCAN_MIXED4=0 gives 8 and 16 lanes per channel (three waves per SIMD),
     // SSM_SCAN_SPLIT=4 or 2 the split launch (states over waves, 4 or 2 per wave, B/C in
@@ -197,7 +197,9 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool conv) {
       };
       const int64_t waves = (int64_t)p.blocks_per_group * groups_or_heads * d->batch;
       const double cost_plain = pass_cost(waves, 4 * kCUs, p.nseg, 1.0);
-      const Cand c80 = candidate(80, 2.6, !split), c48 = candidate(48, 1.9, true);
+      // The 48-channel launch keeps one segment unless segments are forced: with its own
+      // segment count it measured slower than either other launch on every shape tried.
+      const Cand c80 = candidate(80, 2.6, !split), c48 = candidate(48, 1.9, false);
       int rows = 0;   // 0: the plain launch
       if (c80.cost < cost_plain) rows = 80;
       if (c48.cost < std::min(cost_plain, c80.cost)) rows = 48;
