@@ -119,7 +119,7 @@ def cpu_baseline(case, budget_s: float = 12.0, zoh: bool = False, conv=None):
         t = t.contiguous()
         return t.view(torch.int16).numpy().view(np.uint16) if io == "bf16" else t.numpy()
 
-    def run(nb, nch):
+    def run(nb, nch, threads=None):
         """nb batch items; nch channels (BDL) or nch // headdim heads (BLHP)."""
         f = lambda t: None if t is None else t.contiguous().numpy()
         if case.layout == "bdl":
@@ -138,7 +138,7 @@ def cpu_baseline(case, budget_s: float = 12.0, zoh: bool = False, conv=None):
                     f(None if T["delta_bias"] is None else T["delta_bias"][:nh]), case.softplus,
                     f(None if T["h0"] is None else T["h0"][:nb, :nc]))
             elems = nb * case.seqlen * nc * case.dstate
-        threads = oracle.default_threads()
+        threads = threads or oracle.default_threads()
         t0 = time.perf_counter()
         extra = {}
         if conv is not None:                              # the fused input stage, same channels
@@ -161,8 +161,16 @@ def cpu_baseline(case, budget_s: float = 12.0, zoh: bool = False, conv=None):
         nch = min(nch, case.dim)
         what = f"batch item 0, first {nch} of {case.dim} channels"
     dt, el, threads = run(nb, nch)
+    # one thread on about 1/threads of that sample (the first channels of item 0)
+    nch1 = max(probe_ch, (nch * nb) // max(1, threads))
+    if case.layout == "blhp":
+        nch1 = max(case.headdim, (nch1 // case.headdim) * case.headdim)
+    dt1, el1, _ = run(1, min(nch1, case.dim), threads=1)
     return {"value": el / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what}, all {case.seqlen} steps, {case.dstate} states: {el:.3e} elements in {dt:.2f} s"}
+            "sample": f"{what}, all {case.seqlen} steps, {case.dstate} states: {el:.3e} elements in {dt:.2f} s",
+            "value_1thread": el1 / dt1,
+            "sample_1thread": f"batch item 0, first {min(nch1, case.dim)} channels, 1 thread: {el1:.3e} elements in "
+                              f"{dt1:.2f} s"}
 
 
 def decode_bytes(case) -> int:
