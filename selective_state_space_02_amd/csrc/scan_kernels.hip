@@ -21,6 +21,12 @@
 //   B  each wave: the recurrence for its states over the TB steps, B/C read as
 //      wave-uniform LDS broadcasts, partial readout sums into LDS.
 //   C  all threads: sum the NW partial readouts, add D*u, gate, convert, store.
+// The row-group kernels (per-channel layout, N <= 32) instead give each channel LPR
+// lanes of N/LPR states and let every wave run on its own (no workgroup barriers): the
+// plain launch (waves of 8 lanes per channel), the mixed launch (8- and 16-lane waves,
+// 80 channels per workgroup), the two-kind launches (4- or 8-lane waves beside 16-lane
+// ones, 80 or 48 channels per workgroup, one workgroup per CU, the same channels on every
+// SIMD) and the split launch (states over waves, B/C in scalar registers).
 // A sequence cut into time segments runs an aggregate pass first (MODE 1: each
 // segment's decay product exp(A * sum dt) and its end state from a zero start);
 // the main pass (MODE 0) folds the preceding aggregates into its initial state,
