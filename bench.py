@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -82,7 +83,11 @@ def kernel_source_hash(workload: str) -> str:
         kern = "scan_kernels.hip"
     h = hashlib.sha256()
     for f in ("scan_api.cpp", "scan_plan.h", kern):
-        h.update(open(os.path.join(ROOT, "selective_state_space_02_amd", "csrc", f), "rb").read())
+        src = open(os.path.join(ROOT, "selective_state_space_02_amd", "csrc", f), encoding="utf-8").read()
+        # the code only: comments and blank space do not change a kernel
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
