@@ -23,7 +23,7 @@ constexpr int kCUs = 256;   // MI355X compute units
 
 thread_local char g_hip_msg[256] = {0};
 
-int round_up(int64_t x, int64_t m) { return (int)(((x + m - 1) / m) * m); }
+int64_t round_up(int64_t x, int64_t m) { return ((x + m - 1) / m) * m; }
 
 // Segment count: enough parallel units (waves for the row-group kernel, workgroups
 // otherwise) to fill the chip, but no segment shorter than kMinSeg steps.
@@ -133,10 +133,34 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool conv) {
     p.ps = (d->headdim % 32 == 0 && !(ps_env && std::atoi(ps_env) == 16)) ? 32 : 16;
     p.NS = 0; p.NW = 4; p.TB = 64;
     p.grid_rows = (int)(d->headdim / p.ps);
+    // time segments of whole 64-step chunks: an aggregate pass writes each segment's
+    // zero-start end state and decay, the main pass folds them in.  About three workgroups
+    // per CU (two are resident at a time): fewer leave CUs idle or half-loaded, more add
+    // aggregate work (measured on 80 heads of 64 x 128 states, 8192 steps: 1, 2, 3, 4, 6
+    // segments 0.56, 0.59, 0.49, 0.52, 0.52 ms for two sequences; one sequence 0.40 ->
+    // 0.25 ms with 3).  Segments keep at least two chunks.  SSM_SCAN_SEGMENTS forces a count.
     p.nseg = 1;
     p.seg_len = d->seqlen;
+    const int64_t ssd_wgs = (d->headdim / p.ps) * d->nheads * d->batch;
+    int64_t ns = std::min<int64_t>((3 * kCUs + ssd_wgs - 1) / ssd_wgs, std::max<int64_t>(1, d->seqlen / 128));
+    const char* seg_env = std::getenv("SSM_SCAN_SEGMENTS");
+    if (seg_env && *seg_env) ns = std::atoi(seg_env);
+    {
+      ns = std::max<int64_t>(1, ns);
+      int64_t len = round_up((d->seqlen + ns - 1) / ns, 64);
+      ns = (d->seqlen + len - 1) / len;
+      if (ns * d->batch <= 65535) {
+        p.nseg = (int)ns;
+        p.seg_len = len;
+      }
+    }
     p.vec_ok = true;
-    p.seg_bytes = p.bc_bytes = p.ws_bytes = 0;
+    p.bc_bytes = 0;
+    // [seg][b][h] decays (padded to 256 bytes), then [seg][b][h][slice][tile][lane][4] states
+    p.seg_bytes = p.nseg > 1 ? (size_t)round_up((int64_t)(p.nseg - 1) * d->batch * d->nheads * (int64_t)sizeof(float), 256) +
+                                   (size_t)(p.nseg - 1) * (size_t)d->batch * (size_t)d->dim * (size_t)N * sizeof(float)
+                             : 0;
+    p.ws_bytes = p.seg_bytes;
     *pl = p;
     return SSM_OK;
   }
@@ -373,6 +397,10 @@ static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, 
   kp.nblk = pl.nblk;
   kp.wsP = pl.seg_bytes ? (float*)((char*)ws + pl.bc_bytes) : nullptr;
   kp.wsH = pl.seg_bytes ? kp.wsP + half : nullptr;
+  if (pl.kernel == 2 && pl.seg_bytes) {   // chunked multi-head kernel: decays, then states
+    kp.wsP = (float*)ws;
+    kp.wsH = (float*)((char*)ws + ssm::round_up((int64_t)(pl.nseg - 1) * dims->batch * (int64_t)Hn * (int64_t)sizeof(float), 256));
+  }
   kp.L = dims->seqlen; kp.seg_len = pl.seg_len; kp.nseg = pl.nseg;
   kp.batch = (int)dims->batch; kp.dim = (int)dims->dim; kp.N = (int)dims->dstate; kp.Npad = pl.Npad;
   kp.H = (int)Hn; kp.P = bdl ? 1 : (int)dims->headdim; kp.G = (int)dims->ngroups;

@@ -115,7 +115,11 @@ __device__ __forceinline__ bf16x8 ld8_tr_halves(const uint16_t* base, int k0, in
 // Q = 64 steps per chunk, N states (32, 64 or 128), PS positions per workgroup (16 or 32).
 // MFMA lane layout (16x16x32): A row = lane%16, k = 8*(lane/16)+i; B column = lane%16,
 // k = 8*(lane/16)+i; D column = lane%16, rows 4*(lane/16)+r.
-template <int N, int PS, bool ZOH>
+// A sequence cut into time segments of whole chunks runs an aggregate pass first (MODE 1:
+// the state each segment before the last reaches from zero, and its decay e^{A sum dt},
+// the chunk-carry form of the scan operator of «Mamba 选择性状态空间模型» §4.1); the
+// main pass (MODE 0) folds the aggregates of the preceding segments into its initial state.
+template <int N, int PS, bool ZOH, int MODE>
 __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   constexpr int Q = 64;
   // Row strides (elements).  With 16-lane passes, a row stride of 16 B times an odd number
@@ -148,16 +152,18 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   // them so that XCD k runs a contiguous range of (slice, head, batch): the heads of one
   // batch item that share a group's B and C chunks then read them from the same few L2s
   // (measured: HBM reads 2.3x -> 1.1x the algorithmic bytes on 80 heads of 64, 128 states).
-  int pslice, hh, b;
+  int pslice, hh, bz;
   {
     const int nx = gridDim.x, ny = gridDim.y, total = nx * ny * gridDim.z;
     int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
     if (total % 8 == 0) id = (id % 8) * (total / 8) + id / 8;
     pslice = id % nx;
     hh = (id / nx) % ny;
-    b = id / (nx * ny);
+    bz = id / (nx * ny);
   }
+  const int b = bz % p.batch, seg = bz / p.batch;   // batch item, time segment
   const int64_t L = p.L;
+  const int64_t t_seg0 = (int64_t)seg * p.seg_len, t_seg1 = min(L, t_seg0 + p.seg_len);
   const int H = p.H, P = p.P, G = p.G;
   const int g = hh / p.heads_per_group;
   const int p0 = pslice * PS;
@@ -173,10 +179,29 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int n = 16 * tn + 4 * lq + r, q = 16 * tp + l16;
-      hs[i][r] = (k < NST && p.h0) ? p.h0[((int64_t)b * p.dim + (int64_t)hh * P + p0 + q) * N + n] : 0.0f;
+      hs[i][r] = (MODE == 0 && k < NST && p.h0) ? p.h0[((int64_t)b * p.dim + (int64_t)hh * P + p0 + q) * N + n] : 0.0f;
     }
   }
-  auto store_state = [&]() {   // sH[q][n..n+3] = split(state): 8-byte writes
+  // segment aggregates: decays [seg][b][h], states [seg][b][h][slice][tile][lane][r]
+  const int nslice = P / PS;
+  auto agg_state = [&](int s2, int k) __attribute__((always_inline)) {
+    return p.wsH + (((((int64_t)s2 * p.batch + b) * H + hh) * nslice + pslice) * NST + k) * 256 + 4 * lane;
+  };
+  if (MODE == 0) {
+    for (int s2 = 0; s2 < seg; ++s2) {   // fold the preceding segments
+      const float dec = p.wsP[((int64_t)s2 * p.batch + b) * H + hh];
+#pragma unroll
+      for (int i = 0; i < SPW; ++i) {
+        const int k = w + 4 * i;
+        if (k < NST) {
+          const f32x4 a = *(const f32x4*)agg_state(s2, k);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hs[i][r] = fmaf(dec, hs[i][r], a[r]);
+        }
+      }
+    }
+  }
+  auto store_state = [&]() __attribute__((always_inline)) {   // sH[q][n..n+3] = split(state): 8-byte writes
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int k = w + 4 * i, tn = k / PT, tp = k % PT;
@@ -190,7 +215,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
       }
     }
   };
-  store_state();
+  if (MODE == 0) store_state();
 
   const uint16_t* const gB = (const uint16_t*)p.B;
   const uint16_t* const gC = (const uint16_t*)p.C;
@@ -214,16 +239,16 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   // 8 states per lane and contraction step; u and z of this lane's outputs; raw step size
   // of step lane.  Steps past the end load the last valid step (in-bounds, masked later).
   const int64_t last_chunk = ((L - 1) / Q) * Q;
-  u32x4 pB[NBI], pC[NK], pU = {0u, 0u, 0u, 0u};
-  u32x2 pUo[PT], pZo[PT];
-  float pDelta;
+  u32x4 pB[NBI] = {}, pC[NK] = {}, pU = {0u, 0u, 0u, 0u};
+  u32x2 pUo[PT] = {}, pZo[PT] = {};
+  float pDelta = 0.0f;
   // per-lane element offsets of a chunk's loads from its first step, for full chunks and
   // for the last one (its steps past the end load its last valid step: in bounds, masked
   // later); only a uniform chunk base is computed per chunk
   struct Offs {
     uint32_t B[NBI], C, X, XZ, dt;
   };
-  auto offsets = [&](int nv) {
+  auto offsets = [&](int nv) __attribute__((always_inline)) {
     Offs o;
 #pragma unroll
     for (int k = 0; k < NBI; ++k) {
@@ -238,29 +263,34 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
     return o;
   };
   const Offs ofull = offsets(Q), olast = offsets((int)(L - last_chunk));
-  auto prefetch = [&](int64_t tc) {
+  auto prefetch = [&, gB, gC, gU, gDt, gZ, rowBC, rowX, colX, last_chunk, ofull, olast](int64_t tc)
+                      __attribute__((always_inline)) {
     const bool last = tc == last_chunk;
     const int64_t row0 = (int64_t)b * L + tc;    // uniform
     const uint16_t* const bB = gB + row0 * rowBC + (int64_t)g * N;
 #pragma unroll
     for (int k = 0; k < NBI; ++k) pB[k] = *(const u32x4*)(bB + (last ? olast.B[k] : ofull.B[k]));
     const uint16_t* const bC = gC + row0 * rowBC + (int64_t)g * N + (last ? olast.C : ofull.C);
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) pC[kk] = *(const u32x4*)(bC + 32 * kk);
     const uint16_t* const bX = gU + row0 * rowX + colX;
     if (tid < NUI) pU = *(const u32x4*)(bX + (last ? olast.X : ofull.X));
-    const uint32_t oxz = last ? olast.XZ : ofull.XZ;
-    const uint16_t* const bZ = gZ + row0 * rowX + colX;
+    if (MODE == 0) {   // C and the outputs' u and z: the main pass only
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      pUo[j] = *(const u32x2*)(bX + oxz + 16 * j);
-      pZo[j] = *(const u32x2*)(bZ + oxz + 16 * j);
+      for (int kk = 0; kk < NK; ++kk) pC[kk] = *(const u32x4*)(bC + 32 * kk);
+      const uint32_t oxz = last ? olast.XZ : ofull.XZ;
+      const uint16_t* const bZ = gZ + row0 * rowX + colX;
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        pUo[j] = *(const u32x2*)(bX + oxz + 16 * j);
+        pZo[j] = *(const u32x2*)(bZ + oxz + 16 * j);
+      }
     }
     pDelta = bf2f(gDt[row0 * H + hh + (last ? olast.dt : ofull.dt)]);
   };
-  prefetch(0);
+  const int64_t seg_last = ((t_seg1 - 1) / Q) * Q;   // first step of the segment's last chunk
+  prefetch(t_seg0);
+  float lsum = 0.0f;   // aggregate pass: log2 of the segment's decay
 
-  for (int64_t t0 = 0; t0 < L; t0 += Q) {
+  for (int64_t t0 = t_seg0; t0 < t_seg1; t0 += Q) {
     const int nval = (int)min((int64_t)Q, L - t0);
     // ===== stage: B rows; this wave's step sizes and prefix sums; X and w X ===============
 #pragma unroll
@@ -269,13 +299,15 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
       *(u32x4*)&sB[s * BP + nb] = pB[k];
     }
     u32x4 cC[NK];
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) cC[kk] = pC[kk];
     u32x2 cUo[PT], cZo[PT];
+    if (MODE == 0) {
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      cUo[j] = pUo[j];
-      cZo[j] = pZo[j];
+      for (int kk = 0; kk < NK; ++kk) cC[kk] = pC[kk];
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        cUo[j] = pUo[j];
+        cZo[j] = pZo[j];
+      }
     }
     const u32x4 cU = pU;
     {   // every wave computes the chunk's step sizes and prefix sums itself (no barrier)
@@ -297,11 +329,12 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
       sCum[w][lane] = c * A2;     // log2 of the decay from the chunk start through step lane
     }
     // the next chunk's loads fly while this one computes (the last chunk re-reads itself)
-    prefetch(min(t0 + Q, last_chunk));
+    prefetch(min(t0 + Q, seg_last));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const float cum_end = sCum[w][Q - 1];
+    lsum += cum_end;
     if (tid < NUI) {   // X = dt u and w X of one u item, split into hi / lo
       const int s = tid / (PS / 8), qb = (tid % (PS / 8)) * 8;
       float dts = sDt[w][s];
@@ -318,8 +351,10 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
         split2(x0, x1, xh[i], xl[i]);
         split2(x0 * ws, x1 * ws, wh[i], wl[i]);
       }
-      *(u32x4*)&sX[s * XP + qb] = (u32x4){xh[0], xh[1], xh[2], xh[3]};
-      *(u32x4*)&sX[s * XP + PS + qb] = (u32x4){xl[0], xl[1], xl[2], xl[3]};
+      if (MODE == 0) {
+        *(u32x4*)&sX[s * XP + qb] = (u32x4){xh[0], xh[1], xh[2], xh[3]};
+        *(u32x4*)&sX[s * XP + PS + qb] = (u32x4){xl[0], xl[1], xl[2], xl[3]};
+      }
       *(u32x4*)&sXW[s * XP + qb] = (u32x4){wh[0], wh[1], wh[2], wh[3]};
       *(u32x4*)&sXW[s * XP + PS + qb] = (u32x4){wl[0], wl[1], wl[2], wl[3]};
     }
@@ -327,7 +362,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
 
     // ===== wave w: output steps t in [16w, 16w+16) =========================================
     const int ks = 32 * ((w + 2) / 2);   // contraction range over steps covering s <= 16w+15
-    {
+    if (MODE == 0) {
       // M^T = (B C^T) o decay for the step tiles i <= w of this wave's column tile (zeros
       // for i > w inside the range ks), kept in registers as hi / lo bf16 pairs in the
       // layout of the MFMA result (lane: step t, steps s = 16 i + 4 lq + r), which is the
@@ -419,10 +454,19 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
       }
     }
     __syncthreads();   // every wave is done with this chunk's sB, sX, sXW and the old sH
-    store_state();
+    if (MODE == 0) store_state();
+  }
+  if (MODE == 1) {   // the segment's aggregate: its zero-start end state and its decay
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int k = w + 4 * i;
+      if (k < NST) *(f32x4*)agg_state(seg, k) = hs[i];
+    }
+    if (pslice == 0 && tid == 0) p.wsP[((int64_t)seg * p.batch + b) * H + hh] = __builtin_amdgcn_exp2f(lsum);
+    return;
   }
   // ---- final state
-  if (p.h_last) {
+  if (p.h_last && seg == p.nseg - 1) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int k = w + 4 * i, tn = k / PT, tp = k % PT;
@@ -437,12 +481,21 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   }
 }
 
+template <int N, int PS, bool ZOH>
+int launch_ps_z(const KParams& kp, hipStream_t st) {
+  if (kp.nseg > 1) {   // aggregates of the segments before the last
+    hipLaunchKernelGGL((ssd_kernel<N, PS, ZOH, 1>), dim3(kp.P / PS, kp.H, kp.batch * (kp.nseg - 1)), dim3(256), 0, st,
+                       kp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  hipLaunchKernelGGL((ssd_kernel<N, PS, ZOH, 0>), dim3(kp.P / PS, kp.H, kp.batch * kp.nseg), dim3(256), 0, st, kp);
+  return (int)hipGetLastError();
+}
+
 template <int N, int PS>
 int launch_ps(const KParams& kp, int zoh, hipStream_t st) {
-  const dim3 grid(kp.P / PS, kp.H, kp.batch);
-  if (zoh) hipLaunchKernelGGL((ssd_kernel<N, PS, true>), grid, dim3(256), 0, st, kp);
-  else hipLaunchKernelGGL((ssd_kernel<N, PS, false>), grid, dim3(256), 0, st, kp);
-  return (int)hipGetLastError();
+  return zoh ? launch_ps_z<N, PS, true>(kp, st) : launch_ps_z<N, PS, false>(kp, st);
 }
 
 template <int N>

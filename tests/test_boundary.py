@@ -138,7 +138,10 @@ def test_workspace_size_and_plan():
     assert scan.workspace_size(d4) == bc_tile_bytes(1, 131072, 16) + 2 * 7 * 1 * 16 * 2560 * 4
     assert "kernel=rowgroup_mixed4" in scan.describe(d4) and "grid=(32,1,8)" in scan.describe(d4)
     d5 = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
-    assert "kernel=ssd" in scan.describe(d5) and scan.workspace_size(d5) == 0
+    # 320 workgroups: 3 time segments of 43 chunks; two aggregates of (decay per head, state)
+    assert "kernel=ssd" in scan.describe(d5) and "grid=(2,2,3)" in scan.describe(d5)
+    assert "seg_len=2752" in scan.describe(d5)
+    assert scan.workspace_size(d5) == 1280 + 2 * 2 * 5120 * 128 * 4
     d5f = scan.make_dims("blhp", "f32", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
     assert "kernel=workgroup" in scan.describe(d5f) and "NS=16" in scan.describe(d5f)
     d5n = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 100, nheads=80, headdim=64, ngroups=1)
@@ -156,7 +159,7 @@ def test_segment_override_env(monkeypatch):
     monkeypatch.setenv("SSM_SCAN_SEGMENTS", "1")
     assert scan.workspace_size(d) == bc_tile_bytes(4, 2048, 16)       # one segment: the mixed launch
     d = scan.make_dims("blhp", "bf16", 2, 8192, 5120, 128, nheads=80, headdim=64, ngroups=1)
-    assert scan.workspace_size(d) == 0                                 # workgroup kernel, one segment
+    assert scan.workspace_size(d) == 0                                 # chunked kernel, one segment
 
 
 def test_binding_rejects_cpu_tensors():

@@ -117,3 +117,31 @@ def test_ssd_sixteen_positions_per_workgroup(dstate, monkeypatch):
     y_ref, h_ref = oracle_run(c)
     assert err(y2, y_ref) <= TOL and err(h2, h_ref) <= TOL
     assert err(y2, y1.double().cpu().numpy()) <= TOL and err(h2, h1.double().cpu().numpy()) <= TOL
+
+
+@pytest.mark.parametrize("kw,nseg", [
+    (dict(seqlen=1000, dim=128, dstate=128, nheads=2, headdim=64), "3"),       # ragged last chunk
+    (dict(seqlen=640, dim=192, dstate=64, nheads=3, headdim=64, ngroups=3), "5"),
+    (dict(seqlen=257, dim=128, dstate=32, nheads=4, headdim=32), "2"),
+    (dict(seqlen=130, dim=96, dstate=64, nheads=2, headdim=48), "4"),         # 16 positions per workgroup
+    (dict(seqlen=64, dim=128, dstate=128, nheads=2, headdim=64), "3"),        # one chunk: one segment
+])
+def test_ssd_time_segments(kw, nseg, monkeypatch):
+    """Time segments of whole chunks: an aggregate pass (zero-start end state and decay of each
+    segment before the last), then the main pass folding them into each segment's start."""
+    c = make_case("ssd_seg", layout="blhp", io_dtype="bf16", batch=2, seed=kw["seqlen"] + 7, has_h0=True,
+                  A_kind="head_uniform", **kw)
+    y1, h1 = gpu_run(c)
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", nseg)
+    dims = scan.make_dims("blhp", "bf16", c.batch, c.seqlen, c.dim, c.dstate, c.nheads, c.headdim, c.ngroups)
+    txt = scan.describe(dims)
+    assert "kernel=ssd" in txt
+    print(f"[gpu] ssd segments {nseg}: {txt}", flush=True)
+    y2, h2 = gpu_run(c)
+    y_ref, h_ref = oracle_run(c)
+    assert err(y2, y_ref) <= TOL and err(h2, h_ref) <= TOL
+    assert err(y2, y1.double().cpu().numpy()) <= TOL and err(h2, h1.double().cpu().numpy()) <= TOL
+    c.softplus = True
+    y3, h3 = gpu_run(c, "zoh")
+    y3r, h3r = oracle_run(c, "zoh")
+    assert err(y3, y3r) <= TOL and err(h3, h3r) <= TOL
