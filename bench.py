@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 METRIC = "selective-scan elements/s (B·L·D·N) + achieved HBM GB/s vs MI355X peak"
 DEFAULT_WORKLOAD = "mamba2p8b_layer"
 
-# MI355X figures used for the rooflines (vendor numbers).
+# MI355X figures used for the rooflines: vendor peaks; 32 fp32 lanes per SIMD per clock as
+# measured for v_fmac_f32 on gfx950, transcendentals at a quarter of that.
 HBM_PEAK_GBS = 8000.0
 CUS, SIMDS, LANES_PER_CLK, CLOCK_HZ = 256, 4, 32, 2.4e9
 VALU_SLOT_PEAK = CUS * SIMDS * LANES_PER_CLK * CLOCK_HZ       # 78.64e12 fp32 lane-ops/s (= 157.3 TFLOP/s FMA)
@@ -307,7 +308,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the scan shards over "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the scan shards over "
               "batch x channel with no communication); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

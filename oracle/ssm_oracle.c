@@ -36,7 +36,7 @@
  * multi-head SSM).  The readout sums over the state index, as in the
  * page «State Space Models 深度实战：从 S4 到 Mamba 的架构演进与 CUDA 优化» §5.2.
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *  - softplus is evaluated in the overflow-free form max(r,0)+log1p(exp(-|r|)),
  *    which equals log(1+e^r) exactly in real arithmetic;
  *  - SiLU(z) = z / (1 + e^{-z});
