@@ -29,6 +29,7 @@ DEFAULT_WORKLOAD = "mamba2p8b_layer"
 # MI355X figures used for the rooflines: vendor peaks; 32 fp32 lanes per SIMD per clock as
 # measured for v_fmac_f32 on gfx950, transcendentals at a quarter of that.
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak
 CUS, SIMDS, LANES_PER_CLK, CLOCK_HZ = 256, 4, 32, 2.4e9
 VALU_SLOT_PEAK = CUS * SIMDS * LANES_PER_CLK * CLOCK_HZ       # 78.64e12 fp32 lane-ops/s (= 157.3 TFLOP/s FMA)
 TRANS_SLOTS = 4                                               # exp2/log2/rcp issue at 1/4 of the fp32 rate
@@ -58,6 +59,18 @@ def algorithmic_slots(case, zoh=False, conv_k=0) -> float:
     per_head_step = (2 + 2 * TRANS_SLOTS) + (1 + TRANS_SLOTS) + (ZOH_SLOTS if zoh else 0)
     per_chan_step = 2 + ((3 + 2 * TRANS_SLOTS) if has_z else 0)
     return Bsz * L * (Dm * (N * per_elem + per_chan_step) + case.nheads * per_head_step)
+
+
+def ssd_form_flops(case, chunk: int = 64) -> float:
+    """Matrix flops of the chunked (state-space-duality) form of the multi-head layout, counted
+    once: per (b, h, chunk of Q steps) C B^T (Q x Q x N, the causal half), its decayed product
+    with X (Q x Q x P, causal half), the carried state's readout C H (Q x N x P) and the chunk's
+    state contribution B^T X (N x Q x P); FMA = 2 flops.  No operand splitting, no recomputation."""
+    Bsz, L, H, P, N = case.batch, case.seqlen, case.nheads, case.headdim, case.dstate
+    chunks = -(-L // chunk)
+    Q = chunk
+    macs = (Q * Q * N) / 2 + (Q * Q * P) / 2 + Q * N * P + N * Q * P
+    return 2.0 * macs * Bsz * H * chunks
 
 
 def algorithmic_bytes(case) -> int:
@@ -418,6 +431,11 @@ def main():
         "hbm": {"algorithmic_bytes_per_launch": abytes, "achieved_GBs": hbm_gbs, "peak_GBs": HBM_PEAK_GBS,
                 "frac": hbm_gbs / HBM_PEAK_GBS},
     }
+    if "kernel=ssd" in plan:   # the chunked form runs its contractions on bf16 MFMA
+        mf = ssd_form_flops(case) / (launch_ms * 1e-3) / 1e12
+        line["mfma"] = {"achieved": mf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": mf / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": ssd_form_flops(case),
+                        "op": "chunked-form matrix flops, each product counted once (dense bf16 peak)"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget, zoh=args.discretization == "zoh",
                                             conv=None if conv is None else (conv[0].cpu().numpy(),
