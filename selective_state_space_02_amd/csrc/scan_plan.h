@@ -50,8 +50,10 @@ struct KParams {
   const float* h0;
   void* y;
   float* h_last;
-  float* wsP;   // [seg][b][n][d] decay product of each aggregated segment
-  float* wsH;   // [seg][b][n][d] zero-start end state of each aggregated segment
+  float* wsP;   // [seg][b][n][d] decay product of each aggregated segment ([seg][b][h] in the
+                //   chunked multi-head kernel)
+  float* wsH;   // [seg][b][n][d] zero-start end state of each aggregated segment ([seg][b][h]
+                //   [slice][state tile][lane][4] in the chunked multi-head kernel)
   float* bct;   // row-group kernel: [b][g][block] B/C tiles in LDS order (bc_tile_kernel)
   float* bct2;  // split launch: the same tiles per state pair, [b][g][block][pair][t][B C B C]
   const float* conv_w;     // optional input stage (row-group kernels): (dim, conv_k) filters
