@@ -153,8 +153,8 @@ typedef struct ssm_conv {
 
 /*
  * ssm_scan_fwd with the input stage above; x has the layout and dtype of u.
- * Supported for SSM_LAYOUT_BDL with dstate <= 32 (the per-channel kernel);
- * other shapes return SSM_ERR_UNSUPPORTED.  conv or conv->weight NULL:
+ * Supported for SSM_LAYOUT_BDL with dstate <= 32 and seqlen <= 2^26 (the
+ * per-channel kernels); other shapes return SSM_ERR_UNSUPPORTED.  conv or conv->weight NULL:
  * SSM_ERR_NULL_ARG; width outside 1..4: SSM_ERR_UNSUPPORTED.  state_out must
  * not overlap any input or output.  Workspace, stream and errors as for
  * ssm_scan_fwd (ssm_scan_workspace_size gives the scratch size).
