@@ -263,3 +263,29 @@ def test_mixed_launch_override_env(monkeypatch):
     monkeypatch.setenv("SSM_SCAN_SPLIT", "0")
     monkeypatch.setenv("SSM_SCAN_MIXED4", "1")
     assert "kernel=rowgroup_mixed4" in scan.describe(d4) and "grid=(32,1,3)" in scan.describe(d4)
+
+
+def test_plan_segments_and_launch_choices(monkeypatch):
+    """Launch and segment choices of the plan for a few shapes (host logic only)."""
+    for k in ("SSM_SCAN_MIXED", "SSM_SCAN_MIXED4", "SSM_SCAN_SPLIT", "SSM_SCAN_SEGMENTS", "SSM_SCAN_SSD", "SSM_SSD_PS"):
+        monkeypatch.delenv(k, raising=False)
+    # the 48-channel launch keeps one segment unless segments are forced
+    d = dims(batch=16, seqlen=2048, dim=768, dstate=16)
+    assert "kernel=rowgroup_mixed48" in scan.describe(d) and "grid=(16,16,1)" in scan.describe(d)
+    monkeypatch.setenv("SSM_SCAN_MIXED", "48")
+    assert ",1)" in scan.describe(dims(batch=1, seqlen=131072, dim=2560, dstate=16)).split("grid=")[1].split()[0]
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", "3")
+    assert "grid=(54,1,3)" in scan.describe(dims(batch=1, seqlen=131072, dim=2560, dstate=16))
+    monkeypatch.delenv("SSM_SCAN_MIXED")
+    monkeypatch.delenv("SSM_SCAN_SEGMENTS")
+    # chunked multi-head kernel: about three workgroups per CU, segments of at least two chunks
+    mh = lambda B, L, H, P=64, N=128: scan.make_dims("blhp", "bf16", B, L, H * P, N, nheads=H, headdim=P, ngroups=1)
+    assert "grid=(2,1,5)" in scan.describe(mh(1, 8192, 80))          # 160 workgroups -> 5 segments
+    assert "grid=(2,8,1)" in scan.describe(mh(8, 8192, 80))          # 1280 workgroups: one segment
+    assert "grid=(2,1,2)" in scan.describe(mh(1, 256, 8))            # 256 steps: at most 2 segments
+    assert "grid=(2,1,1)" in scan.describe(mh(1, 100, 8))            # under two chunks: one segment
+    d = mh(1, 8192, 80)
+    nseg = 5
+    assert scan.workspace_size(d) == (nseg - 1) * 80 * 4 + (nseg - 1) * 1 * 80 * 64 * 128 * 4   # decays, states
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", "1")
+    assert "grid=(2,1,1)" in scan.describe(d) and scan.workspace_size(d) == 0
