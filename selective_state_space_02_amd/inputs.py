@@ -2,8 +2,9 @@
 
 This module only draws random numbers and shapes tensors; it holds none of the
 scan's arithmetic, so both the HIP path and the fp64 oracle may use it.
-Everything is generated on the CPU with a seeded torch.Generator, drawn in
-float32 and rounded to bfloat16 (round-to-nearest-even) where the case says so.
+Everything is generated with a seeded torch.Generator, on the CPU unless a case
+asks for another device (cases too large to draw on the host), drawn in float32
+and rounded to bfloat16 (round-to-nearest-even) where the case says so.
 The step sizes come from the inverse of log(1+e^r); that inverse is the only
 formula here and it only places the drawn values inside the wanted range.
 
@@ -49,26 +50,32 @@ class Case:
         return self.batch * self.seqlen * self.dim * self.dstate
 
 
-def _gen(seed: int) -> torch.Generator:
-    g = torch.Generator(device="cpu")
+def _gen(seed: int, device="cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
     g.manual_seed(seed)
     return g
 
 
 def _normal(shape, g, std=1.0):
-    return torch.randn(*shape, generator=g, dtype=torch.float32) * std
+    return torch.randn(*shape, generator=g, dtype=torch.float32, device=g.device) * std
 
 
 def _uniform(shape, g, lo, hi):
-    return torch.rand(*shape, generator=g, dtype=torch.float32) * (hi - lo) + lo
+    return torch.rand(*shape, generator=g, dtype=torch.float32, device=g.device) * (hi - lo) + lo
+
+
+_RESAMPLE_CHUNK = 1 << 28   # masked assignment is done per chunk (torch's fails past 2^31 elements)
 
 
 def _truncated_normal(shape, g, clip):
-    x = torch.randn(*shape, generator=g, dtype=torch.float32)
-    bad = x.abs() > clip
-    while bool(bad.any()):
-        x[bad] = torch.randn(int(bad.sum()), generator=g, dtype=torch.float32)
-        bad = x.abs() > clip
+    x = torch.randn(*shape, generator=g, dtype=torch.float32, device=g.device)
+    flat = x.view(-1)
+    for s in range(0, flat.numel(), _RESAMPLE_CHUNK):
+        part = flat[s:s + _RESAMPLE_CHUNK]
+        bad = part.abs() > clip
+        while bool(bad.any()):
+            part[bad] = torch.randn(int(bad.sum()), generator=g, dtype=torch.float32, device=g.device)
+            bad = part.abs() > clip
     return x
 
 
@@ -83,8 +90,8 @@ def _io(x: torch.Tensor, io_dtype: str) -> torch.Tensor:
 
 def make_case(name="custom", *, layout="bdl", io_dtype="bf16", batch=1, seqlen=256, dim=64, dstate=16,
               nheads=0, headdim=0, ngroups=1, seed=1, has_z=True, has_D=True, has_bias=True,
-              softplus=True, has_h0=False, A_kind="arange", delta_kind="small") -> Case:
-    """General seeded case.
+              softplus=True, has_h0=False, A_kind="arange", delta_kind="small", device="cpu") -> Case:
+    """General seeded case (tensors on `device`; the draws depend on the device's generator).
 
     A_kind: "arange" -> A[d, n] = -(n+1); "lognormal" -> -exp(N(0, 0.5));
             "head_uniform" -> per head -exp(U(0, 2.7)).
@@ -93,7 +100,7 @@ def make_case(name="custom", *, layout="bdl", io_dtype="bf16", batch=1, seqlen=2
                            step near 1e-4 and the rest in [1e-2, 1e-1] (no bias);
                            "zero" -> raw = 0; "wide" -> raw ~ N(0, 3), bias 0.
     """
-    g = _gen(seed)
+    g = _gen(seed, device)
     c = Case(name, layout, io_dtype, batch, seqlen, dim, dstate, nheads, headdim, ngroups, softplus)
     T = {}
     N = dstate
@@ -116,18 +123,18 @@ def make_case(name="custom", *, layout="bdl", io_dtype="bf16", batch=1, seqlen=2
         if bias is None:
             raw = raw + (_BIAS_LO + _BIAS_HI) / 2
     elif delta_kind == "long":
-        mask = torch.rand(*dts, generator=g) < 0.1
+        mask = torch.rand(*dts, generator=g, device=g.device) < 0.1
         lo_s, hi_s = math.log(5e-5), math.log(2e-4)
         lo_l, hi_l = math.log(1e-2), math.log(1e-1)
         tgt = torch.where(mask, torch.exp(_uniform(dts, g, lo_s, hi_s)), torch.exp(_uniform(dts, g, lo_l, hi_l)))
         raw = _inv_softplus(tgt)
         bias = None
     elif delta_kind == "zero":
-        raw = torch.zeros(dts)
-        bias = torch.zeros(nbias) if has_bias else None
+        raw = torch.zeros(dts, device=g.device)
+        bias = torch.zeros(nbias, device=g.device) if has_bias else None
     elif delta_kind == "wide":
         raw = _normal(dts, g, 3.0)
-        bias = torch.zeros(nbias) if has_bias else None
+        bias = torch.zeros(nbias, device=g.device) if has_bias else None
     else:
         raise ValueError(delta_kind)
     T["delta"] = _io(raw, io_dtype)
@@ -135,7 +142,7 @@ def make_case(name="custom", *, layout="bdl", io_dtype="bf16", batch=1, seqlen=2
     # A
     if layout == "bdl":
         if A_kind == "arange":
-            A = -torch.arange(1, N + 1, dtype=torch.float32).repeat(dim, 1)
+            A = -torch.arange(1, N + 1, dtype=torch.float32, device=g.device).repeat(dim, 1)
         elif A_kind == "lognormal":
             A = -torch.exp(_normal((dim, N), g, 0.5))
         else:
