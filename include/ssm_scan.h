@@ -51,6 +51,9 @@
  * nonzero, the library allocates it stream-ordered (hipMallocAsync /
  * hipFreeAsync on `stream`); otherwise dims->workspace must hold at least
  * that many bytes (SSM_ERR_WORKSPACE if dims->workspace_bytes is smaller).
+ * With a caller workspace (or a zero size) a call enqueues kernel launches
+ * only (no allocation, no memset, no copy), so it may be captured in a HIP
+ * graph; the graph then reads and writes the same addresses on every replay.
  *
  * Errors: every entry point returns SSM_OK (0) or a negative code; no C++
  * exception crosses the ABI.  ssm_strerror(code) gives a static message; for

@@ -8,6 +8,7 @@ call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Tuple
 
@@ -148,6 +149,19 @@ def _check(t: Optional[torch.Tensor], name: str, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _on_stream(fn):
+    """With stream= given, allocate the outputs and the internal workspace under that stream, so
+    torch's caching allocator reuses their memory only in that stream's order."""
+    @functools.wraps(fn)
+    def run(*args, stream: Optional[torch.cuda.Stream] = None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return run
+
+
+@_on_stream
 def ssm_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
                  D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                  delta_bias: Optional[torch.Tensor] = None, softplus: bool = True,
@@ -221,6 +235,7 @@ def call_update_raw(x, delta, A, B, C, D, z, delta_bias, softplus, h_in, h_out, 
                                               y, ctypes.byref(dims), stream))
 
 
+@_on_stream
 def ssm_state_update(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
                      D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                      delta_bias: Optional[torch.Tensor] = None, softplus: bool = True,
@@ -285,6 +300,7 @@ def call_conv_raw(x, conv: Conv, delta, A, B, C, D, z, delta_bias, softplus, h0,
                                                stream))
 
 
+@_on_stream
 def ssm_conv_scan_fwd(x: torch.Tensor, conv_weight: torch.Tensor, conv_bias: Optional[torch.Tensor],
                       delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
                       D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
