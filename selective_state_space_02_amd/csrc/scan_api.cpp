@@ -78,7 +78,8 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool conv) {
     rows_per_group = d->dim / d->ngroups;
     groups_or_heads = d->ngroups;
   } else {
-    if (d->nheads < 1 || d->headdim < 1 || d->nheads * d->headdim != d->dim) return SSM_ERR_BAD_DIMS;
+    if (d->nheads < 1 || d->headdim < 1 || d->nheads > d->dim || d->headdim > d->dim) return SSM_ERR_BAD_DIMS;
+    if (d->nheads * d->headdim != d->dim) return SSM_ERR_BAD_DIMS;   // no overflow: both <= dim <= 2^30
     if (d->nheads % d->ngroups) return SSM_ERR_BAD_DIMS;
     rows_per_group = d->headdim;
     groups_or_heads = d->nheads;

@@ -80,7 +80,8 @@ def test_bad_dims_bdl(kw):
 
 
 @pytest.mark.parametrize("kw", [dict(nheads=3, headdim=64), dict(nheads=0, headdim=64), dict(nheads=2, headdim=0),
-                                dict(nheads=2, headdim=64, ngroups=3)])
+                                dict(nheads=2, headdim=64, ngroups=3),
+                                dict(nheads=1 << 62, headdim=1 << 62), dict(nheads=-(1 << 62), headdim=-2)])
 def test_bad_dims_blhp(kw):
     d = dict(layout="blhp", dim=128)
     d.update(kw)
