@@ -1,0 +1,97 @@
+"""Host code of the library under the undefined-behaviour and integer-overflow sanitizers.
+
+The argument checks and the launch planner (scan_api.cpp) are rebuilt with
+-fsanitize=undefined,integer in trap mode (host code only; the device objects
+are the ones build() made), then, in a child process so that a trap fails the
+test instead of ending pytest:
+  * the boundary tests run against that build (every error path, no GPU);
+  * a seeded fuzz feeds ssm_scan_workspace_size and ssm_scan_describe random and
+    extreme dimensions (zero, negative, 2^26, 2^30, 2^31, 2^40, 2^62, INT64_MAX ...):
+    signed or unsigned overflow, bad shifts or truncating conversions would trap.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "selective_state_space_02_amd")
+OBJS = [os.path.join(PKG, "_build", f) for f in ("scan_kernels_delta_b.o", "scan_kernels_zoh.o", "update_kernels.o",
+                                                 "ssd_kernels.o")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FUZZ = r'''
+import ctypes, random, sys
+sys.path.insert(0, sys.argv[1])
+import selective_state_space_02_amd.scan as s
+s._LIB_PATH = sys.argv[2]
+lib = s.load_library()
+rng = random.Random(int(sys.argv[3]))
+vals = [0, 1, 2, 3, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000, 2048, 5120, 65535,
+        65536, 1 << 20, 1 << 26, (1 << 26) + 1, 1 << 30, (1 << 30) + 1, 1 << 31, 1 << 40, (1 << 40) + 1, 1 << 62,
+        (1 << 63) - 1, -1, -(1 << 63)]
+def pick():
+    return rng.choice(vals) if rng.random() < 0.7 else rng.randrange(1, 1 << rng.choice([4, 8, 12, 16, 24, 32, 40]))
+buf = ctypes.create_string_buffer(256)
+valid = 0
+for _ in range(int(sys.argv[4])):
+    d = s.Dims(pick(), pick(), pick(), pick(), pick(), pick(), pick(), rng.choice([0, 1, 2, -1]), rng.choice([0, 1, 5]),
+               None, 0)
+    d.discretization = rng.choice([0, 1, 2])
+    r = rng.random()
+    if r < 0.4:      # well-formed multi-head sizes
+        d.layout, d.io_dtype = 1, rng.choice([0, 1])
+        d.nheads, d.headdim = rng.choice([1, 2, 8, 80, 1 << 20]), rng.choice([1, 8, 16, 64, 100])
+        d.dim, d.ngroups = d.nheads * d.headdim, rng.choice([1, 2, d.nheads])
+        d.dstate = rng.choice([16, 32, 64, 128, 256, 48, 300])
+        d.batch, d.seqlen = rng.choice([1, 2, 65535]), rng.choice([1, 64, 8192, 1 << 26, 1 << 40])
+    elif r < 0.8:    # well-formed channel-layout sizes
+        d.layout, d.io_dtype = 0, rng.choice([0, 1])
+        d.ngroups = rng.choice([1, 2, 4])
+        d.dim = d.ngroups * rng.choice([1, 80, 2560, 1 << 28])
+        d.dstate = rng.choice([1, 8, 16, 24, 32, 64, 256])
+        d.batch = rng.choice([1, 4, 65535])
+        d.seqlen = rng.choice([1, 2, 31, 2048, 131072, (1 << 26) + 5, 1 << 40])
+    lib.ssm_scan_workspace_size(ctypes.byref(d))
+    valid += lib.ssm_scan_describe(ctypes.byref(d), buf, 256) == 0
+print("valid plans", valid)
+'''
+
+
+@pytest.fixture(scope="module")
+def sanitized_lib(tmp_path_factory):
+    if not os.path.exists(HIPCC) or not all(os.path.exists(o) for o in OBJS):
+        pytest.skip("hipcc or the built device objects are missing (run build() first)")
+    d = tmp_path_factory.mktemp("ubsan")
+    obj = str(d / "scan_api.o")
+    lib = str(d / "libssm_scan.so")
+    # host code only: every sanitizer flag goes to the host compilation
+    cc = [HIPCC, "-O1", "-g", "-std=c++17", "-fPIC", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host",
+          "-fsanitize=integer", "-Xarch_host", "-fsanitize-trap=all", "-I", os.path.join(ROOT, "include"), "-I",
+          os.path.join(PKG, "csrc"), "-c", os.path.join(PKG, "csrc", "scan_api.cpp"), "-o", obj]
+    r = subprocess.run(cc, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib, obj, *OBJS], capture_output=True,
+                       text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    yield lib
+    shutil.rmtree(str(d), ignore_errors=True)
+
+
+def test_boundary_tests_under_sanitizers(sanitized_lib):
+    code = (f"import sys; sys.path.insert(0, {ROOT!r}); import selective_state_space_02_amd.scan as s; "
+            f"s._LIB_PATH = {sanitized_lib!r}; import pytest; "
+            f"raise SystemExit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', '-m', 'not gpu', "
+            f"{os.path.join(ROOT, 'tests', 'test_boundary.py')!r}]))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 0, (r.returncode, r.stdout[-2000:], r.stderr[-2000:])
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_plan_fuzz_under_sanitizers(sanitized_lib, seed):
+    r = subprocess.run([sys.executable, "-c", FUZZ, ROOT, sanitized_lib, str(seed), "40000"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, (r.returncode, r.stdout[-2000:], r.stderr[-2000:])
+    assert int(r.stdout.split()[-1]) > 1000, r.stdout
