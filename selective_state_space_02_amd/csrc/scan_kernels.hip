@@ -177,14 +177,20 @@ struct BF16IO {
 };
 
 // ------------------------------------------------------------ elementwise math
-// softplus(r) = log(1 + e^r) = max(r, 0) + log1p(e^-|r|), with log1p(e) taken as
-// ln 2 * log2(1 + e).  1 + e lies in [1, 2], so nothing overflows; rounding 1 + e
-// leaves an absolute error of about 2^-24 in the step size, which is far below the
-// step sizes whose value matters (the step only enters the state through dt*u*B and
-// exp(dt*A), both of which vanish with dt).
+// softplus(r) = log(1 + e^r) = max(r, 0) + log1p(e), e = e^-|r| in (0, 1], with
+// log1p(e) taken as ln 2 * log2(w), w = fl(1 + e) in [1, 2] (nothing overflows).
+// Rounding 1 + e costs an absolute error of up to 2^-24 in the step, i.e. a relative
+// error of about 2^-24 / dt for small steps (6e-5 at dt = 1e-3).  With float32 storage
+// (ACC) the rounding error e - (w - 1) is added back (w - 1 is exact for w in [1, 2]),
+// which leaves a few ulp.  With bfloat16 storage the inputs themselves carry a relative
+// rounding of 2^-9, far above the uncorrected error for steps down to 1e-4.
+template <bool ACC>
 __device__ __forceinline__ float softplus_f(float r) {
   const float e = __builtin_amdgcn_exp2f(-fabsf(r) * kLog2e);
-  return fmaf(__builtin_amdgcn_logf(1.0f + e), kLn2, r > 0.0f ? r : 0.0f);
+  const float w = 1.0f + e;
+  float base = r > 0.0f ? r : 0.0f;
+  if (ACC) base += e - (w - 1.0f);
+  return fmaf(__builtin_amdgcn_logf(w), kLn2, base);
 }
 
 // SiLU(z) = z / (1 + e^-z)
@@ -385,7 +391,7 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
           for (int q = 0; q < VEC; ++q) {
             const bool ok = rok && t0 + q < nvalid;
             const float rr = raw[q] + br;
-            const float dt = ok ? (p.softplus ? softplus_f(rr) : rr) : 0.0f;
+            const float dt = ok ? (p.softplus ? softplus_f<IO::kBytes == 4>(rr) : rr) : 0.0f;
             dtv[q] = dt;
             duv[q] = dt * uu[q];
             keep_u[k * VEC + q] = uu[q];
@@ -410,7 +416,7 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
         if (t < TB) {
           const bool tok = t < nvalid;
           const float rr = IO::cvt(pm_dt[k]) + bias_head;
-          const float dt = tok ? (p.softplus ? softplus_f(rr) : rr) : 0.0f;
+          const float dt = tok ? (p.softplus ? softplus_f<IO::kBytes == 4>(rr) : rr) : 0.0f;
           const float uu = IO::cvt(pm_u[k]);
           keep_u[k] = uu;
           keep_z[k] = IO::cvt(pm_z[k]);
@@ -810,7 +816,7 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
     for (int q = 0; q < QPL; ++q) {
       const bool ok = QPL * k + q < nvalid;
       const float rr = raw[q] + bias;
-      const float sp = softplus_f(rr);                        // branch-free: the steps interleave
+      const float sp = softplus_f<IO::kBytes == 4>(rr);   // branch-free: the steps interleave
       const float dt = ok ? (use_sp ? sp : rr) : 0.0f;
       dtv[q] = dt;
       duv[q] = dt * uu[q];
@@ -1186,7 +1192,7 @@ __device__ __forceinline__ void split_state_wave(const KParams& p, int g, int rb
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
       const float rr = raw[q] + bias;
-      const float sp = softplus_f(rr);
+      const float sp = softplus_f<IO::kBytes == 4>(rr);
       const float dt = QS * qi + q < nvalid ? (p.softplus ? sp : rr) : 0.0f;
       dtv[q] = dt;
       duv[q] = dt * uu[q];

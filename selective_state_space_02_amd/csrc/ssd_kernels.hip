@@ -63,7 +63,9 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
   lo = pack_bf(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
-// softplus(r) = max(r, 0) + ln 2 * log2(1 + 2^(-|r| log2 e)); 1 + e in [1, 2] never overflows
+// softplus(r) = max(r, 0) + ln 2 * log2(1 + 2^(-|r| log2 e)); 1 + e in [1, 2] never overflows.
+// Rounding 1 + e costs a relative error of about 2^-24 / dt in small steps, far below the
+// 2^-9 rounding of the bfloat16 inputs this kernel reads.
 __device__ __forceinline__ float softplus_s(float r) {
   const float e = __builtin_amdgcn_exp2f(-fabsf(r) * kLog2e);
   return fmaf(__builtin_amdgcn_logf(1.0f + e), kLn2, r > 0.0f ? r : 0.0f);
