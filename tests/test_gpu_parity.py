@@ -151,6 +151,22 @@ def test_optional_arguments(opts, layout):
     check_case(c)
 
 
+@pytest.mark.parametrize("A_mode", ["zero", "huge_negative"])
+@pytest.mark.parametrize("layout,io", [("bdl", "f32"), ("bdl", "bf16"), ("blhp", "f32"), ("blhp", "bf16")])
+def test_degenerate_decays(layout, io, A_mode):
+    """A = 0 (no decay: the state is a running sum of dt*u*B) and A = -1e4 (the state keeps
+    almost nothing of its past), on the row-group, workgroup and chunked kernels."""
+    kw = dict(io_dtype=io, batch=2, seqlen=300, seed=43, has_h0=True)
+    if layout == "bdl":
+        kw.update(layout="bdl", dim=160, dstate=16, A_kind="lognormal")
+    else:
+        kw.update(layout="blhp", dim=256, dstate=64, nheads=4, headdim=64)
+    c = make_case("degenerate", **kw)
+    A = c.tensors["A"]
+    c.tensors["A"] = torch.zeros_like(A) if A_mode == "zero" else torch.full_like(A, -1e4)
+    check_case(c)
+
+
 def test_no_h_last_output():
     c = make_case("noh", layout="bdl", io_dtype="bf16", batch=1, seqlen=64, dim=64, dstate=16, seed=5)
     y, h = gpu_run(c, want_h_last=False)
