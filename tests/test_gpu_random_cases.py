@@ -1,9 +1,11 @@
 """GPU parity over seeded random combinations of shape, options and launch.
 
-Each case draws a layout, storage type, batch, length, channel count, state count, groups,
-optional arguments (gate, D, bias, initial state, no softplus), step-size regime, the
-discretization, the fused input stage, and a forced launch shape or time-segment count, then
-compares y and h_last with the fp64 oracle under the usual bounds (1e-4 float32, 2e-2
+Each case draws a layout, storage type, batch, length, channel count, state count (1 to
+256), groups, optional arguments (gate, D, bias, initial state, no softplus), step-size regime
+(small, wide, long-sequence, zero), the discretization, the fused input stage (with or without
+a carried state, whose output is compared bit for bit), a single decode step (in place or not)
+and a forced launch shape or time-segment count, then compares y and h_last with the fp64
+oracle under the usual bounds (1e-4 float32, 2e-2
 bfloat16, relative to 1 + |ref|).  Without softplus the step is delta itself (no bias), kept
 positive.  The draws are fixed by the seed, so the cases are the same on every run.
 """
@@ -45,8 +47,8 @@ def draw(rng, big):
     L = rng.choice([1, 2, 7, 31, 32, 33, 64, 95, 128, 200, 257, 500, 1000] + ([2048, 3001, 4096] if big else []))
     conv, env = 0, {}
     if layout == "bdl":
-        N = rng.choice([16, 16, 16, 8, 13, 32, 24, 64])
-        G = rng.choice([1, 1, 2])
+        N = rng.choice([16, 16, 16, 8, 13, 32, 24, 64, 128, 256, 1, 2])
+        G = rng.choice([1, 1, 2, 4])
         D = G * rng.choice([1, 3, 8, 16, 40, 48, 80, 81, 100, 160, 170] + ([240, 481] if big else []))
         H = P = 0
         if N <= 32 and rng.random() < 0.3:
@@ -57,22 +59,24 @@ def draw(rng, big):
         if rng.random() < 0.15 and not conv:
             env["SSM_SCAN_SPLIT"] = rng.choice(["2", "4"])
     else:
-        N = rng.choice([32, 64, 128, 16, 48])
+        N = rng.choice([32, 64, 128, 16, 48, 256, 1])
         G = rng.choice([1, 2])
         H = G * rng.choice([1, 2, 3])
-        P = rng.choice([16, 32, 48, 64, 8])
+        P = rng.choice([16, 32, 48, 64, 8, 128, 3])
         D = H * P
         if rng.random() < 0.2:
             env["SSM_SCAN_SSD"] = "0"
         if rng.random() < 0.2:
             env["SSM_SSD_PS"] = "16"
     if rng.random() < 0.3:
-        env["SSM_SCAN_SEGMENTS"] = str(rng.choice([1, 2, 3, 5]))
+        env["SSM_SCAN_SEGMENTS"] = str(rng.choice([1, 2, 3, 5, 9]))
     return dict(layout=layout, io=io, B=B, L=L, D=D, N=N, G=G, H=H, P=P, conv=conv, env=env,
                 disc=rng.choice(["delta_b", "delta_b", "zoh"]),
                 opts=dict(has_z=rng.random() < 0.7, has_D=rng.random() < 0.8, has_bias=rng.random() < 0.8,
-                          has_h0=rng.random() < 0.6, delta_kind=rng.choice(["small", "small", "wide", "long"])),
-                softplus=rng.random() < 0.85, seed=rng.randrange(1 << 20))
+                          has_h0=rng.random() < 0.6,
+                          delta_kind=rng.choice(["small", "small", "wide", "long", "zero"])),
+                softplus=rng.random() < 0.85, seed=rng.randrange(1 << 20), decode=rng.random() < 0.15,
+                inplace=rng.random() < 0.5, conv_state=rng.random() < 0.5)
 
 
 def run_case(k, monkeypatch):
@@ -82,9 +86,11 @@ def run_case(k, monkeypatch):
         if v:
             monkeypatch.setenv(key, v)
     layout, io = k["layout"], k["io"]
-    c = make_case("random", layout=layout, io_dtype=io, batch=k["B"], seqlen=k["L"], dim=k["D"], dstate=k["N"],
-                  nheads=k["H"], headdim=k["P"], ngroups=k["G"], seed=k["seed"],
-                  A_kind="head_uniform" if layout == "blhp" else "lognormal", **k["opts"])
+    decode = k["decode"]
+    opts = dict(k["opts"], has_h0=True) if decode else k["opts"]
+    c = make_case("random", layout=layout, io_dtype=io, batch=k["B"], seqlen=1 if decode else k["L"], dim=k["D"],
+                  dstate=k["N"], nheads=k["H"], headdim=k["P"], ngroups=k["G"], seed=k["seed"],
+                  A_kind="head_uniform" if layout == "blhp" else "lognormal", **opts)
     c.softplus = k["softplus"]
     if not c.softplus:   # the step is delta itself: positive and small
         c.tensors["delta"] = (c.tensors["delta"].float().abs() * 0.05).to(c.tensors["delta"].dtype)
@@ -93,24 +99,41 @@ def run_case(k, monkeypatch):
     T = {key: (None if v is None else v.to(dev)) for key, v in c.tensors.items()}
     f = lambda key: None if c.tensors[key] is None else c.tensors[key].numpy()
     kw = dict(layout=layout, io_dtype=io, ngroups=k["G"], discretization="zoh" if k["disc"] == "zoh" else "euler")
-    if k["conv"]:
+    cs = cs_ref = None
+    if decode:   # one step on the carried state h0: the step's inputs are the sequence's only step
+        first = (lambda t: None if t is None else t[:, :, 0].contiguous()) if layout == "bdl" else \
+                (lambda t: None if t is None else t[:, 0].contiguous())
+        bc = (lambda t: t[..., 0].contiguous()) if layout == "bdl" else (lambda t: t[:, 0].contiguous())
+        h_in = T["h0"].clone()
+        yq, h = scan.ssm_state_update(first(T["u"]), first(T["delta"]), T["A"], bc(T["B"]), bc(T["C"]), T["D"],
+                                      first(T["z"]), T["delta_bias"], c.softplus, h_in, layout=layout,
+                                      inplace=k["inplace"], discretization=k["disc"])
+        y = yq.unsqueeze(2) if layout == "bdl" else yq.unsqueeze(1)
+    elif k["conv"]:
+        K = k["conv"]
         g = torch.Generator().manual_seed(k["seed"])
-        cw = (torch.randn(k["D"], k["conv"], generator=g) * 0.5).contiguous()
+        cw = (torch.randn(k["D"], K, generator=g) * 0.5).contiguous()
         cb = (torch.randn(k["D"], generator=g) * 0.2).contiguous()
-        y, h, _ = scan.ssm_conv_scan_fwd(T["u"], cw.to(dev), cb.to(dev), T["delta"], T["A"], T["B"], T["C"], T["D"],
-                                         T["z"], T["delta_bias"], c.softplus, T["h0"], discretization=k["disc"])
-        kw.update(conv_w=cw.numpy(), conv_b=cb.numpy())
+        csi = torch.randn(k["B"], k["D"], K - 1, generator=g).contiguous() if K > 1 and k["conv_state"] else None
+        y, h, cs = scan.ssm_conv_scan_fwd(T["u"], cw.to(dev), cb.to(dev), T["delta"], T["A"], T["B"], T["C"], T["D"],
+                                          T["z"], T["delta_bias"], c.softplus, T["h0"], discretization=k["disc"],
+                                          conv_state_in=None if csi is None else csi.to(dev), want_conv_state=True)
+        kw.update(conv_w=cw.numpy(), conv_b=cb.numpy(), conv_state_in=None if csi is None else csi.numpy(),
+                  want_conv_state=True)
     else:
         y, h = scan.ssm_scan_fwd(T["u"], T["delta"], T["A"], T["B"], T["C"], T["D"], T["z"], T["delta_bias"],
                                  c.softplus, T["h0"], layout=layout, discretization=k["disc"])
     torch.cuda.synchronize()
-    yr, hr = oracle.scan_f64(np_io(c.tensors["u"], io), np_io(c.tensors["delta"], io), f("A"),
-                             np_io(c.tensors["B"], io), np_io(c.tensors["C"], io), f("D"), np_io(c.tensors["z"], io),
-                             f("delta_bias"), c.softplus, f("h0"), **kw)[:2]
+    res = oracle.scan_f64(np_io(c.tensors["u"], io), np_io(c.tensors["delta"], io), f("A"),
+                          np_io(c.tensors["B"], io), np_io(c.tensors["C"], io), f("D"), np_io(c.tensors["z"], io),
+                          f("delta_bias"), c.softplus, f("h0"), **kw)
+    yr, hr = res[:2]
+    if cs is not None:   # the input stage's final state is a copy of raw inputs: exact
+        assert np.array_equal(cs.double().cpu().numpy(), np.asarray(res[2], dtype=np.float64).reshape(tuple(cs.shape)))
     return scaled_err(y, yr), scaled_err(h, hr)
 
 
-@pytest.mark.parametrize("seed,count,big", [(7, 150, False), (23, 60, True)])
+@pytest.mark.parametrize("seed,count,big", [(7, 150, False), (23, 60, True), (41, 150, False)])
 def test_random_cases(seed, count, big, monkeypatch):
     rng = random.Random(seed)
     bad = []
