@@ -154,3 +154,39 @@ def test_graph_decode_steps_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref), f"token {tok}: y differs"
         assert torch.equal(state, ref_state), f"token {tok}: state differs"
+
+
+def test_concurrent_threads_and_streams():
+    """Host threads calling the library at once (ctypes releases the GIL), each on its own stream
+    with its own workspace, give the results of serial calls bit for bit."""
+    import threading
+    names = ["rowgroup", "ssd", "workgroup_f32", "rowgroup"]
+    cases = [make_case(n, seed=930 + i, **CASES[n]) for i, n in enumerate(names)]
+    Ts = [on_device(c) for c in cases]
+    serial = [run_scan(c, T) for c, T in zip(cases, Ts)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in cases]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    out = [None] * len(cases)
+    errors = []
+
+    def worker(i):
+        try:
+            res = []
+            for _ in range(5):
+                res.append(run_scan(cases[i], Ts[i], stream=streams[i]))
+            out[i] = res
+        except Exception as e:   # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (y0, h0), res in zip(serial, out):
+        for y, h in res:
+            assert torch.equal(y, y0) and torch.equal(h, h0)
