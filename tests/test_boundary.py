@@ -290,3 +290,49 @@ def test_plan_segments_and_launch_choices(monkeypatch):
     assert scan.workspace_size(d) == (nseg - 1) * 80 * 4 + (nseg - 1) * 1 * 80 * 64 * 128 * 4   # decays, states
     monkeypatch.setenv("SSM_SCAN_SEGMENTS", "1")
     assert "grid=(2,1,1)" in scan.describe(d) and scan.workspace_size(d) == 0
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "ssm_scan.h"
+int main(void) {
+  ssm_dims_t d;
+  char buf[256];
+  memset(&d, 0, sizeof d);
+  d.batch = 4; d.seqlen = 2048; d.dim = 5120; d.dstate = 16; d.ngroups = 1;
+  d.layout = SSM_LAYOUT_BDL; d.io_dtype = SSM_BF16;
+  if (ssm_scan_version() <= 0) return 1;
+  if (ssm_scan_describe(&d, buf, sizeof buf) != SSM_OK || strncmp(buf, "kernel=", 7) != 0) return 2;
+  if (ssm_scan_workspace_size(&d) == 0) return 3;           /* the B/C tiles */
+  d.dim = 0;
+  if (ssm_scan_describe(&d, buf, sizeof buf) != SSM_ERR_BAD_DIMS) return 4;
+  if (strlen(ssm_strerror(SSM_ERR_BAD_DIMS)) == 0) return 5;
+  if (ssm_scan_fwd(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, NULL, NULL, NULL, &d, NULL) != SSM_ERR_NULL_ARG)
+    return 6;
+  printf("ok %s\n", ssm_strerror(SSM_OK));
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_a_c_program_links(tmp_path):
+    """The boundary is a C ABI: the header compiles as strict C99 and C++, and a C program
+    linked against the library calls its host-side entry points (no GPU needed)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None or shutil.which("g++") is None:
+        pytest.skip("no host compiler")
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    inc = os.path.join(ROOT, "include")
+    r = subprocess.run(["g++", "-std=c++11", "-Wall", "-Werror", "-x", "c++", "-I", inc, "-c", str(src), "-o",
+                        str(tmp_path / "caller_cxx.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    libdir = os.path.dirname(scan.library_path())
+    exe = str(tmp_path / "caller")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc, str(src), "-L", libdir,
+                        "-lssm_scan", f"-Wl,-rpath,{libdir}", "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), (r.returncode, r.stdout, r.stderr)
