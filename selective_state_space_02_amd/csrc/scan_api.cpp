@@ -63,7 +63,7 @@ bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u); }
 
 }  // namespace
 
-int make_plan(const ssm_dims_t* d, Plan* pl, bool conv) {
+int make_plan(const ssm_dims_t* d, Plan* pl) {
   if (!d || !pl) return SSM_ERR_NULL_ARG;
   if (d->layout != SSM_LAYOUT_BDL && d->layout != SSM_LAYOUT_BLHP) return SSM_ERR_UNSUPPORTED;
   if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
@@ -182,15 +182,8 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool conv) {
     // per step.  Two workgroup sizes: 80 channels (4 lanes x 4 states, and 16 lanes x 1
     // state; about 2.6 plain waves of work per SIMD) and 48 channels (8 lanes x 2 states,
     // and 16 x 1; about 1.9).  The 80-channel one picks its own segment count.  SSM_SCAN_MIXED=0 forces
-    // the plain launch, 1 the 80-channel one, 48 the 48-channel one (tests, tuning).  For
-    // 80 channels SSM_SCAN_MIXED4=0 gives 8 and 16 lanes per channel (three waves per SIMD),
-    // SSM_SCAN_SPLIT=4 or 2 the split launch (states over waves, 4 or 2 per wave, B/C in
-    // scalar registers, two workgroup barriers per block, one segment only; its tiles take
-    // twice the workspace).  Both measured slower on MI355X: the first spends more
-    // instructions and LDS traffic per element, the second stalls at its barriers.
+    // the plain launch, 1 the 80-channel one, 48 the 48-channel one (tests, tuning).
     if (p.Npad == 16) {
-      const char* senv = std::getenv("SSM_SCAN_SPLIT");
-      const bool split = !conv && senv && (*senv == '2' || *senv == '4');   // no input stage in the split launch
       const char* seg_env = std::getenv("SSM_SCAN_SEGMENTS");
       const bool seg_forced = seg_env && *seg_env;
       const int64_t L = d->seqlen;
@@ -224,24 +217,18 @@ int make_plan(const ssm_dims_t* d, Plan* pl, bool conv) {
       const double cost_plain = pass_cost(waves, 4 * kCUs, p.nseg, 1.0);
       // The 48-channel launch keeps one segment unless segments are forced: with its own
       // segment count it measured slower than either other launch on every shape tried.
-      const Cand c80 = candidate(80, 2.6, !split), c48 = candidate(48, 1.9, false);
+      const Cand c80 = candidate(80, 2.6, true), c48 = candidate(48, 1.9, false);
       int rows = 0;   // 0: the plain launch
       if (c80.cost < cost_plain) rows = 80;
       if (c48.cost < std::min(cost_plain, c80.cost)) rows = 48;
       const char* env = std::getenv("SSM_SCAN_MIXED");
       if (env && *env) rows = *env == '0' ? 0 : std::atoi(env) == 48 ? 48 : 80;
-      if (split && rows == 80 && c80.nseg != 1) rows = 0;   // the split launch runs one segment
       const Cand& c = rows == 48 ? c48 : c80;
       if (rows && groups_or_heads * c.blocks <= 0x7fffffff) {
-        const char* m4env = std::getenv("SSM_SCAN_MIXED4");
-        const bool mixed4 = !(m4env && *m4env == '0');
-        p.kernel = rows == 48 ? 6 : split ? 4 : mixed4 ? 5 : 3;
-        p.ps = p.kernel == 4 ? *senv - '0' : 0;   // split launch: states per state wave
+        p.kernel = rows == 48 ? 6 : 5;
         if (p.kernel == 5) p.vec_ok = p.vec_ok && d->seqlen % 8 == 0;   // 8-step vectors
-        if (p.kernel == 4 && p.ps == 4) p.vec_ok = p.vec_ok && d->seqlen % 8 == 0;   // 8-step vectors
         p.blocks_per_group = (int)c.blocks;
         p.grid_rows = (int)(groups_or_heads * c.blocks);
-        if (p.kernel == 4) p.bc_bytes *= 2;
         if (c.nseg != p.nseg) {   // the two-kind launch's own segment count
           int64_t len = round_up((L + c.nseg - 1) / c.nseg, p.TB);
           p.seg_len = len;
@@ -296,18 +283,16 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
   if (buf && buf_len) {
     std::snprintf(buf, buf_len,
                   "kernel=%s layout=%s io=%s disc=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d "
-                  "ws=%zu%s",
+                  "ws=%zu",
                   p.kernel == 6   ? "rowgroup_mixed48"
                   : p.kernel == 5 ? "rowgroup_mixed4"
-                  : p.kernel == 4 ? "rowgroup_split"
-                  : p.kernel == 3 ? "rowgroup_mixed"
                   : p.kernel == 2 ? "ssd"
                   : p.kernel == 1 ? "rowgroup"
                                   : "workgroup",
                   p.layout == SSM_LAYOUT_BDL ? "bdl" : "blhp",
                   p.io == SSM_BF16 ? "bf16" : "f32", p.disc == SSM_DISC_ZOH ? "zoh" : "delta_b", p.NS, p.NW, p.TB,
                   p.Npad, p.grid_rows, (long long)dims->batch, p.nseg, (long long)p.seg_len, (int)p.vec_ok,
-                  p.ws_bytes, p.kernel == 4 ? (p.ps == 2 ? " states_per_wave=2" : " states_per_wave=4") : "");
+                  p.ws_bytes);
   }
   return SSM_OK;
 }
@@ -318,7 +303,7 @@ static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, 
   ssm::g_hip_msg[0] = 0;
   if (!u || !delta || !A || !B || !C || !y || !dims) return SSM_ERR_NULL_ARG;
   ssm::Plan pl;
-  int rc = ssm::make_plan(dims, &pl, conv != nullptr);
+  int rc = ssm::make_plan(dims, &pl);
   if (rc != SSM_OK) return rc;
   const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, y, h_last};
   for (const void* q : ptrs)
@@ -327,7 +312,7 @@ static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, 
     if (!conv->weight) return SSM_ERR_NULL_ARG;
     if (conv->width < 1 || conv->width > 4 || conv->reserved != 0) return SSM_ERR_UNSUPPORTED;
     // the fused stage lives in the per-channel (row-group) kernels
-    if (pl.kernel != 1 && pl.kernel != 3 && pl.kernel != 5 && pl.kernel != 6) return SSM_ERR_UNSUPPORTED;
+    if (pl.kernel != 1 && pl.kernel != 5 && pl.kernel != 6) return SSM_ERR_UNSUPPORTED;
     const void* cps[] = {conv->weight, conv->bias, conv->state_in, conv->state_out};
     for (const void* q : cps)
       if (ssm::misaligned(q)) return SSM_ERR_ALIGN;
@@ -394,7 +379,6 @@ static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, 
   kp.h0 = h0; kp.y = y; kp.h_last = h_last;
   const size_t half = pl.seg_bytes / 2 / sizeof(float);
   kp.bct = pl.bc_bytes ? (float*)ws : nullptr;
-  kp.bct2 = pl.kernel == 4 ? (float*)((char*)ws + pl.bc_bytes / 2) : nullptr;   // second half of the tiles
   kp.nblk = pl.nblk;
   kp.wsP = pl.seg_bytes ? (float*)((char*)ws + pl.bc_bytes) : nullptr;
   kp.wsH = pl.seg_bytes ? kp.wsP + half : nullptr;

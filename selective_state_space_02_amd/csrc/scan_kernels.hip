@@ -23,10 +23,9 @@
 //   C  all threads: sum the NW partial readouts, add D*u, gate, convert, store.
 // The row-group kernels (per-channel layout, N <= 32) instead give each channel LPR
 // lanes of N/LPR states and let every wave run on its own (no workgroup barriers): the
-// plain launch (waves of 8 lanes per channel), the mixed launch (8- and 16-lane waves,
-// 80 channels per workgroup), the two-kind launches (4- or 8-lane waves beside 16-lane
-// ones, 80 or 48 channels per workgroup, one workgroup per CU, the same channels on every
-// SIMD) and the split launch (states over waves, B/C in scalar registers).
+// plain launch (waves of 8 lanes per channel) and the two-kind launches (4- or 8-lane
+// waves beside 16-lane ones, 80 or 48 channels per workgroup, one workgroup per CU, the
+// same channels on every SIMD).
 // A sequence cut into time segments runs an aggregate pass first (MODE 1: each
 // segment's decay product exp(A * sum dt) and its end state from a zero start);
 // the main pass (MODE 0) folds the preceding aggregates into its initial state,
@@ -178,18 +177,15 @@ struct BF16IO {
 
 // ------------------------------------------------------------ elementwise math
 // softplus(r) = log(1 + e^r) = max(r, 0) + log1p(e), e = e^-|r| in (0, 1], with
-// log1p(e) taken as ln 2 * log2(w), w = fl(1 + e) in [1, 2] (nothing overflows).
-// Rounding 1 + e costs an absolute error of up to 2^-24 in the step, i.e. a relative
-// error of about 2^-24 / dt for small steps (6e-5 at dt = 1e-3).  With float32 storage
-// (ACC) the rounding error e - (w - 1) is added back (w - 1 is exact for w in [1, 2]),
-// which leaves a few ulp.  With bfloat16 storage the inputs themselves carry a relative
-// rounding of 2^-9, far above the uncorrected error for steps down to 1e-4.
-template <bool ACC>
+// log1p(e) taken as ln 2 * log2(w) + (e - (w - 1)), w = fl(1 + e) in [1, 2] (nothing
+// overflows; w - 1 is exact).  The second term puts back the rounding of 1 + e, which
+// would otherwise be an absolute error of up to 2^-24 in the step, i.e. a relative error
+// of about 2^-24 / dt in small steps (6e-5 at dt = 1e-3, 1e-3 at 5e-5) scaling every
+// dt * u * B term and the decay; with it a few ulp remain.
 __device__ __forceinline__ float softplus_f(float r) {
   const float e = __builtin_amdgcn_exp2f(-fabsf(r) * kLog2e);
   const float w = 1.0f + e;
-  float base = r > 0.0f ? r : 0.0f;
-  if (ACC) base += e - (w - 1.0f);
+  const float base = (r > 0.0f ? r : 0.0f) + (e - (w - 1.0f));
   return fmaf(__builtin_amdgcn_logf(w), kLn2, base);
 }
 
@@ -391,7 +387,7 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
           for (int q = 0; q < VEC; ++q) {
             const bool ok = rok && t0 + q < nvalid;
             const float rr = raw[q] + br;
-            const float dt = ok ? (p.softplus ? softplus_f<IO::kBytes == 4>(rr) : rr) : 0.0f;
+            const float dt = ok ? (p.softplus ? softplus_f(rr) : rr) : 0.0f;
             dtv[q] = dt;
             duv[q] = dt * uu[q];
             keep_u[k * VEC + q] = uu[q];
@@ -416,7 +412,7 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
         if (t < TB) {
           const bool tok = t < nvalid;
           const float rr = IO::cvt(pm_dt[k]) + bias_head;
-          const float dt = tok ? (p.softplus ? softplus_f<IO::kBytes == 4>(rr) : rr) : 0.0f;
+          const float dt = tok ? (p.softplus ? softplus_f(rr) : rr) : 0.0f;
           const float uu = IO::cvt(pm_u[k]);
           keep_u[k] = uu;
           keep_z[k] = IO::cvt(pm_z[k]);
@@ -632,8 +628,6 @@ namespace rg {
 constexpr int TB = 32;          // steps per block
 constexpr int TP = TB + 4;      // padded LDS row stride
 constexpr int WPG = 4;          // waves per workgroup of the plain launch (independent; packing only)
-constexpr int MIX_WAVES = 12;   // mixed launch: 8 waves of 8 lanes per channel, then 4 of 16
-constexpr int MIX_ROWS = 80;    // channels per mixed workgroup
 constexpr int TILE = 64 * TP;   // dt|du tile, later the partial sums (one row of TP per lane)
 template <int NPAD> constexpr int bc_tile() { return TB * 2 * NPAD; }   // floats per B/C tile
 }  // namespace rg
@@ -648,10 +642,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // B_t, C_t of one (batch item, group, time block) as the tile the row-group kernel
 // copies into LDS: [t (32)][n (N_pad)][B C], fp32, zero for states >= N and steps >= L.
 // Grid (time blocks, G, batch).
-// With SPLIT > 0, also the same values per group of SPLIT states for the split launch:
-// [group (N_pad/SPLIT)][t (32)][B_n C_n for the group's states], so that one wave reads
-// the values of its states for four steps with 64-byte scalar loads.
-template <typename IO, int NPAD, int SPLIT = 0>
+template <typename IO, int NPAD>
 __global__ void __launch_bounds__(256) bc_tile_kernel(KParams p) {
   using namespace rg;
   constexpr int TILE_BC = bc_tile<NPAD>();
@@ -669,23 +660,13 @@ __global__ void __launch_bounds__(256) bc_tile_kernel(KParams p) {
       cv = IO::cvt(IO::ld_bits(p.C, s));
     }
     *(float2*)(dst + (t * NPAD + n) * 2) = make_float2(bv, cv);
-    if (SPLIT) *(float2*)(p.bct2 + tile + (n / SPLIT) * (TB * 2 * SPLIT) + (t * SPLIT + n % SPLIT) * 2) = make_float2(bv, cv);
   }
 }
 
-// LDS-only workgroup barrier: every wave's LDS writes before it are visible after it
-__device__ __forceinline__ void wg_lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // The body of one wave: channels r0 .. r0+64/LPR-1 of group g (clamped at the group's end).
-// BAR: the wave takes part in two workgroup barriers per time block (split launch).
 // SPF / HZF: softplus on the step and the z gate fixed at compile time (0/1), or -1 to
 // read them from the parameters.
-template <typename IO, int LPR, int NS, int MODE, bool VECOK, bool CONV, bool BAR = false, int SPF = -1,
-          int HZF = -1>
+template <typename IO, int LPR, int NS, int MODE, bool VECOK, bool CONV, int SPF = -1, int HZF = -1>
 __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, float* s_tile, float* s_bc) {
   using namespace rg;
   constexpr int RPW = 64 / LPR;                              // channels per wave
@@ -816,7 +797,7 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
     for (int q = 0; q < QPL; ++q) {
       const bool ok = QPL * k + q < nvalid;
       const float rr = raw[q] + bias;
-      const float sp = softplus_f<IO::kBytes == 4>(rr);   // branch-free: the steps interleave
+      const float sp = softplus_f(rr);   // branch-free: the steps interleave
       const float dt = ok ? (use_sp ? sp : rr) : 0.0f;
       dtv[q] = dt;
       duv[q] = dt * uu[q];
@@ -831,7 +812,7 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
       *(float2*)&s_dt[row * TP + 2 * k] = make_float2(dtv[0], dtv[1]);
       *(float2*)&s_du[row * TP + 2 * k] = make_float2(duv[0], duv[1]);
     }
-    if constexpr (BAR) wg_lds_barrier(); else wave_lds_sync();
+    wave_lds_sync();
 
     // The recurrence over the 32 steps for this lane's NS states.  Software
     // pipelined by groups of 4 steps: the LDS operands of group g+1 are read while
@@ -919,7 +900,7 @@ __device__ __forceinline__ void rowgroup_wave(const KParams& p, int g, int r0, f
       for (int t4 = 0; t4 < TB; t4 += 4)
         *(float4*)&s_part[(row * LPR + k) * TP + t4] =
             make_float4(part[t4], part[t4 + 1], part[t4 + 2], part[t4 + 3]);
-      if constexpr (BAR) wg_lds_barrier(); else wave_lds_sync();
+      wave_lds_sync();
       // sum of the channel's LPR partials of this lane's steps, as a pairwise tree
       float pv[LPR][QPL];
 #pragma unroll
@@ -1062,27 +1043,6 @@ rowgroup_kernel(KParams p) {
                                               s_tile[wv], s_bc[wv]);
 }
 
-// mixed launch (16 states): waves 0..7 take 8 channels each with 8 lanes per channel,
-// waves 8..11 take 4 channels each with 16 lanes per channel; 80 channels per workgroup
-template <typename IO, int MODE, bool VECOK, bool CONV>
-__global__ void __launch_bounds__(rg::MIX_WAVES * 64) rowgroup_mixed_kernel(KParams p) {
-  using namespace rg;
-  __shared__ __attribute__((aligned(16))) float s_tile[MIX_WAVES][TILE];
-  __shared__ __attribute__((aligned(16))) float s_bc[MIX_WAVES][bc_tile<16>()];
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = blockIdx.x / p.blocks_per_group;
-  const int rbase = (blockIdx.x % p.blocks_per_group) * MIX_ROWS;
-  if (wv < 8) {
-    const int r0 = rbase + 8 * wv;
-    if (r0 >= p.rows_per_group) return;                      // no barriers: idle waves may leave
-    rowgroup_wave<IO, 8, 2, MODE, VECOK, CONV>(p, g, r0, s_tile[wv], s_bc[wv]);
-  } else {
-    const int r0 = rbase + 64 + 4 * (wv - 8);
-    if (r0 >= p.rows_per_group) return;
-    rowgroup_wave<IO, 16, 1, MODE, VECOK, CONV>(p, g, r0, s_tile[wv], s_bc[wv]);
-  }
-}
-
 // Two-kind launches (16 states), one workgroup per CU: waves 0..3 take 64/LPRA channels each
 // with LPRA lanes of 16/LPRA states per channel, waves 4..7 take 4 channels each with 16
 // lanes per channel; waves w and w+4 share a SIMD, so every SIMD holds the same channels.
@@ -1103,285 +1063,11 @@ __global__ void __launch_bounds__(8 * 64) rowgroup_pair_kernel(KParams p) {
   if (wv < 4) {
     const int r0 = rbase + (64 / LPRA) * wv;
     if (r0 >= p.rows_per_group) return;                      // no barriers: idle waves may leave
-    rowgroup_wave<IO, LPRA, 16 / LPRA, MODE, VECOK, CONV, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
+    rowgroup_wave<IO, LPRA, 16 / LPRA, MODE, VECOK, CONV, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
   } else {
     const int r0 = rbase + 4 * (64 / LPRA) + 4 * (wv - 4);
     if (r0 >= p.rows_per_group) return;
-    rowgroup_wave<IO, 16, 1, MODE, VECOK, CONV, false, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
-  }
-}
-
-// Split launch (16 states, 80 channels per workgroup, one workgroup per CU).
-// 16/NSW "state waves" hold 64 channels, one channel per lane, each wave NSW of the 16
-// states: all lanes of a wave then use the same B_t, C_t, which come from 64-byte scalar
-// loads and enter the arithmetic as SGPR operands; nothing of the recurrence goes through
-// LDS except each channel's step size and dt*u, computed once per workgroup (the state
-// waves' threads share out the block's 64 x 32 channel-steps, QS consecutive steps of one
-// channel each) and read back by every state wave, and the state waves' readout partials,
-// summed by the threads that produced the step sizes.  Four more waves take 16 channels
-// with 16 lanes per channel (the 16-lane body of the mixed launch).  The hardware places
-// wave w on the same SIMD as waves w+4 and w+8, so every SIMD holds the same share of both
-// kinds: equal work per SIMD.  Two workgroup barriers per time block (after the step sizes,
-// after the partials); the 16-lane waves take part in both.
-namespace rg {
-template <int NSW>
-struct SplitLds {
-  static constexpr int NWS = 16 / NSW;   // state waves
-  float dt[64][TP];                      // step size per channel and step of the block
-  float du[64][TP];                      // dt * u
-  float part[NWS][64][TP];               // readout partial of each state wave
-  float tile16[4][TILE];                 // 16-lane waves: their own tiles
-  float bc16[4][bc_tile<16>()];
-};
-}  // namespace rg
-
-template <typename IO, bool VECOK, int NSW>
-__device__ __forceinline__ void split_state_wave(const KParams& p, int g, int rbase, int w, rg::SplitLds<NSW>& S) {
-  using namespace rg;
-  typedef float f32x16 __attribute__((ext_vector_type(16)));
-  typedef __attribute__((address_space(4))) const f32x16 cf32x16;
-  constexpr int NWS = 16 / NSW;               // state waves
-  constexpr int QS = 32 * 64 / (NWS * 64);    // channel-steps per io thread and block (4 or 8)
-  constexpr int TPC = TB / QS;                // io threads per channel
-  constexpr int NBC = NSW / 2;                // 16-float scalar loads per group of 4 steps
-  constexpr int kB = IO::kBytes;
-  constexpr int NCH = QS * kB / 16 > 0 ? QS * kB / 16 : 1;     // 16-byte chunks per tensor and block
-  using RawC = typename RawT<QS * kB / NCH>::T;
-  static_assert(NSW == 2 || NSW == 4, "two or four states per wave");
-  const int lane = threadIdx.x & 63;
-  const int b = blockIdx.y;
-  const int64_t L = p.L;
-  const int rows_in = min(64, p.rows_per_group - rbase);     // >= 1
-  // state role: channel cc (one per lane); io role: channel ci, steps QS*qi .. QS*qi+QS-1.
-  // Lanes past the last channel repeat the last one (identical values, identical places).
-  const int tid = w * 64 + lane;
-  const int cc = min(lane, rows_in - 1);
-  const int ci = min(tid / TPC, rows_in - 1);
-  const int qi = tid % TPC;
-  const int dbase = g * p.rows_per_group + rbase;
-  const int dc = dbase + cc, di = dbase + ci;
-
-  float A2[NSW], h[NSW];
-#pragma unroll
-  for (int j = 0; j < NSW; ++j) {
-    const int n = NSW * w + j;
-    A2[j] = n < p.N ? p.A[(int64_t)dc * p.N + n] * kLog2e : 0.0f;
-    h[j] = (p.h0 && n < p.N) ? p.h0[((int64_t)b * p.dim + dc) * p.N + n] : 0.0f;
-  }
-  const float bias = p.bias ? p.bias[di] : 0.0f;
-  const float Dd = p.D ? p.D[di] : 0.0f;
-
-  const int64_t ioff = (((int64_t)b * p.dim + di) * L + QS * qi) * kB;   // this thread's steps of its channel
-  const char* const pu = (const char*)p.u + ioff;
-  const char* const pdl = (const char*)p.delta + ioff;
-  const char* const pz = (const char*)p.zsrc + ioff;
-  char* const py = (char*)p.y + ioff;
-  // this wave's B/C values: [block][t][B_n C_n for its NSW states]; one group of 4 steps
-  // is NBC consecutive 16-float loads
-  cf32x16* const tiles =
-      (cf32x16*)(p.bct2 + (int64_t)(b * p.G + g) * p.nblk * bc_tile<16>() + w * (TB * 2 * NSW));
-  constexpr int TILE16 = bc_tile<16>() / 16;   // 16-float units per block tile
-
-  // pb: the scalar B/C of the first groups of this block on entry, of the next block on exit
-  constexpr int AHEAD = NSW == 2 ? 2 : 1;      // groups requested together, that many groups ahead
-  constexpr int NPB = AHEAD * NBC;
-  auto run_block = [&](int64_t tb, int nvalid, const float (&raw)[QS], const float (&uu)[QS], const float (&zz)[QS],
-                       f32x16 (&pb)[NPB]) {
-    // ---- step sizes and dt*u of this thread's QS steps, shared with the state waves
-    float dtv[QS], duv[QS];
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      const float rr = raw[q] + bias;
-      const float sp = softplus_f<IO::kBytes == 4>(rr);
-      const float dt = QS * qi + q < nvalid ? (p.softplus ? sp : rr) : 0.0f;
-      dtv[q] = dt;
-      duv[q] = dt * uu[q];
-    }
-#pragma unroll
-    for (int q = 0; q < QS; q += 4) {
-      *(float4*)&S.dt[ci][QS * qi + q] = make_float4(dtv[q], dtv[q + 1], dtv[q + 2], dtv[q + 3]);
-      *(float4*)&S.du[ci][QS * qi + q] = make_float4(duv[q], duv[q + 1], duv[q + 2], duv[q + 3]);
-    }
-    const cf32x16* tl = tiles + (tb / TB) * TILE16;
-    const cf32x16* tn = tb + TB < L ? tl + TILE16 : tl;   // next block's tile (none after the last)
-    wg_lds_barrier();
-
-    // ---- the recurrence of this wave's states of channel cc over the block's 32 steps.
-    // Scalar loads and LDS reads share one wait counter and a wait for a scalar load
-    // waits for everything outstanding, so the B/C and step sizes of AHEAD groups are
-    // requested together, AHEAD groups before their use.
-    constexpr int NG = TB / 4;
-    float part[TB];
-    f32x16 bc[NG][NBC];
-    float4 gdt[NG], gdu[NG];
-#pragma unroll
-    for (int j = 0; j < AHEAD; ++j) {
-#pragma unroll
-      for (int m = 0; m < NBC; ++m) bc[j][m] = pb[j * NBC + m];
-      gdt[j] = *(const float4*)&S.dt[cc][4 * j];
-      gdu[j] = *(const float4*)&S.du[cc][4 * j];
-    }
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      __builtin_amdgcn_sched_barrier(0);   // keep each group's requests where they are written
-      if (gi % AHEAD == 0 && gi + AHEAD < NG) {
-#pragma unroll
-        for (int j = gi + AHEAD; j < gi + 2 * AHEAD; ++j) {
-#pragma unroll
-          for (int m = 0; m < NBC; ++m) bc[j][m] = tl[j * NBC + m];
-          gdt[j] = *(const float4*)&S.dt[cc][4 * j];
-          gdu[j] = *(const float4*)&S.du[cc][4 * j];
-        }
-      }
-      if (gi == NG - AHEAD) {
-#pragma unroll
-        for (int m = 0; m < NPB; ++m) pb[m] = tn[m];
-      }
-      const float dq[4] = {gdt[gi].x, gdt[gi].y, gdt[gi].z, gdt[gi].w};
-      const float uq[4] = {gdu[gi].x, gdu[gi].y, gdu[gi].z, gdu[gi].w};
-      float a[4][NSW], x[4][NSW];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int j = 0; j < NSW; ++j) {
-          // step q, state j: B at 2*(NSW*q + j), C right after it, within the group's loads
-          const int o = 2 * (NSW * q + j);
-          const float y = dq[q] * A2[j];
-          a[q][j] = __builtin_amdgcn_exp2f(y);
-          x[q][j] = uq[q] * bc[gi][o / 16][o % 16];
-          if (kZOH) x[q][j] *= zoh_factor(y, a[q][j]);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NSW; ++j) {
-          const int o = 2 * (NSW * q + j) + 1;
-          h[j] = fmaf(a[q][j], h[j], x[q][j]);
-          acc = j == 0 ? bc[gi][o / 16][o % 16] * h[j] : fmaf(bc[gi][o / 16][o % 16], h[j], acc);
-        }
-        part[4 * gi + q] = acc;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t4 = 0; t4 < TB; t4 += 4)
-      *(float4*)&S.part[w][cc][t4] = make_float4(part[t4], part[t4 + 1], part[t4 + 2], part[t4 + 3]);
-    wg_lds_barrier();
-
-    // ---- readout of this thread's QS steps: the state waves' partials, D*u, gate
-    float pv[NWS][QS];
-#pragma unroll
-    for (int k = 0; k < NWS; ++k)
-#pragma unroll
-      for (int q = 0; q < QS; q += 4) {
-        const float4 v = *(const float4*)&S.part[k][ci][QS * qi + q];
-        pv[k][q] = v.x; pv[k][q + 1] = v.y; pv[k][q + 2] = v.z; pv[k][q + 3] = v.w;
-      }
-#pragma unroll
-    for (int m = NWS / 2; m >= 1; m /= 2)
-#pragma unroll
-      for (int k = 0; k < m; ++k)
-#pragma unroll
-        for (int q = 0; q < QS; ++q) pv[k][q] += pv[k + m][q];
-    float ys[QS];
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      float yv = fmaf(Dd, uu[q], pv[0][q]);
-      if (p.has_z) yv *= silu_f(zz[q]);
-      ys[q] = yv;
-    }
-    char* const yb = py + tb * kB;
-    if (VECOK && nvalid == TB) {
-#pragma unroll
-      for (int q = 0; q < QS; q += 4) IO::template stv_stream<4>(yb + q * kB, ys + q);
-    } else {
-#pragma unroll
-      for (int q = 0; q < QS; ++q)
-        if (QS * qi + q < nvalid) IO::st(yb, q, ys[q]);
-    }
-  };
-
-  // ------------------------------------------------- full blocks, prefetched
-  int64_t t_blk = 0;
-  f32x16 pb[NPB];
-#pragma unroll
-  for (int m = 0; m < NPB; ++m) pb[m] = tiles[m];
-  if (VECOK) {
-    const int64_t n_full = L / TB;
-    RawC pf_dt[NCH], pf_u[NCH], pf_z[NCH];
-    auto issue = [&](int64_t tb) {
-      const int64_t ob = tb * kB;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        pf_dt[c] = ((const RawC*)(pdl + ob))[c];
-        pf_u[c] = ((const RawC*)(pu + ob))[c];
-        pf_z[c] = ((const RawC*)(pz + ob))[c];
-      }
-    };
-    if (n_full > 0) issue(0);
-    // vmcnt(0) before the loop: inside it, the wait for a prefetch then only has to
-    // cover the loads issued before the previous block's y store, not the store
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    for (int64_t it = 0; it < n_full; ++it, t_blk += TB) {
-      float raw[QS], uu[QS], zz[QS];
-      constexpr int PER = QS / NCH;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        IO::template unpack<PER>(pf_dt[c], raw + c * PER);
-        IO::template unpack<PER>(pf_u[c], uu + c * PER);
-        IO::template unpack<PER>(pf_z[c], zz + c * PER);
-      }
-      issue(it + 1 < n_full ? t_blk + TB : t_blk);   // the last one re-reads this block (unused)
-      run_block(t_blk, TB, raw, uu, zz, pb);
-    }
-  }
-  // ------------------------------------------ remaining steps, element loads
-  for (; t_blk < L; t_blk += TB) {
-    const int nvalid = (int)min((int64_t)TB, L - t_blk);
-    const int64_t ob = t_blk * kB;
-    float raw[QS], uu[QS], zz[QS];
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      const int64_t i = QS * qi + q < nvalid ? q : -QS * qi;   // clamped to step t_blk of the row
-      raw[q] = IO::cvt(IO::ld_bits(pdl + ob, i));
-      uu[q] = IO::cvt(IO::ld_bits(pu + ob, i));
-      zz[q] = IO::cvt(IO::ld_bits(pz + ob, i));
-    }
-    run_block(t_blk, nvalid, raw, uu, zz, pb);
-  }
-
-  if (p.h_last && lane < rows_in) {
-#pragma unroll
-    for (int j = 0; j < NSW; ++j) {
-      const int n = NSW * w + j;
-      if (n < p.N) p.h_last[((int64_t)b * p.dim + dc) * p.N + n] = h[j];
-    }
-  }
-}
-
-template <typename IO, bool VECOK, int NSW>
-__global__ void __launch_bounds__((16 / NSW + 4) * 64) rowgroup_split_kernel(KParams p) {
-  using namespace rg;
-  constexpr int NWS = 16 / NSW;
-  __shared__ __attribute__((aligned(16))) SplitLds<NSW> S;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = blockIdx.x / p.blocks_per_group;
-  const int rbase = (blockIdx.x % p.blocks_per_group) * MIX_ROWS;
-  if (wv < NWS) {
-    split_state_wave<IO, VECOK, NSW>(p, g, rbase, wv, S);
-  } else {
-    const int r0 = rbase + 64 + 4 * (wv - NWS);
-    if (r0 < p.rows_per_group) {
-      rowgroup_wave<IO, 16, 1, 0, VECOK, false, true>(p, g, r0, S.tile16[wv - NWS], S.bc16[wv - NWS]);
-    } else {
-      // no channels: keep the barrier count of the others (two per time block)
-      for (int64_t t = 0; t < p.L; t += TB) {
-        wg_lds_barrier();
-        wg_lds_barrier();
-      }
-    }
+    rowgroup_wave<IO, 16, 1, MODE, VECOK, CONV, SPF, HZF>(p, g, r0, s_tile[wv], s_bc[wv]);
   }
 }
 
@@ -1437,39 +1123,6 @@ int launch_rowgroup(const Plan& pl, const KParams& kp, hipStream_t st) {
   return launch_rowgroup_modes<IO, NS, false, false>(pl, kp, st);
 }
 
-template <typename IO, bool VECOK, bool CONV>
-int launch_rowgroup_mixed_c(const KParams& kp, hipStream_t st) {
-  hipLaunchKernelGGL((bc_tile_kernel<IO, 16>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
-  const int gx = kp.blocks_per_group * kp.G;
-  if (kp.nseg > 1) {
-    hipLaunchKernelGGL((rowgroup_mixed_kernel<IO, 1, VECOK, CONV>), dim3(gx, kp.batch, kp.nseg - 1),
-                       dim3(rg::MIX_WAVES * 64), 0, st, kp);
-    e = hipGetLastError();
-    if (e != hipSuccess) return (int)e;
-  }
-  hipLaunchKernelGGL((rowgroup_mixed_kernel<IO, 0, VECOK, CONV>), dim3(gx, kp.batch, kp.nseg),
-                     dim3(rg::MIX_WAVES * 64), 0, st, kp);
-  return (int)hipGetLastError();
-}
-
-template <typename IO, bool VECOK>
-int launch_rowgroup_mixed(const KParams& kp, hipStream_t st) {
-  return kp.conv_k > 0 ? launch_rowgroup_mixed_c<IO, VECOK, true>(kp, st)
-                       : launch_rowgroup_mixed_c<IO, VECOK, false>(kp, st);
-}
-
-template <typename IO, bool VECOK, int NSW>
-int launch_rowgroup_split(const KParams& kp, hipStream_t st) {
-  hipLaunchKernelGGL((bc_tile_kernel<IO, 16, NSW>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL((rowgroup_split_kernel<IO, VECOK, NSW>), dim3(kp.blocks_per_group * kp.G, kp.batch, 1),
-                     dim3((16 / NSW + 4) * 64), 0, st, kp);
-  return (int)hipGetLastError();
-}
-
 template <typename IO, int LPRA, bool VECOK, int SPF, int HZF, bool CONV>
 int launch_rowgroup_pair_f(const KParams& kp, hipStream_t st) {
   hipLaunchKernelGGL((bc_tile_kernel<IO, 16>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
@@ -1508,18 +1161,6 @@ int launch_io(const Plan& pl, const KParams& kp, hipStream_t st) {
   if (LAYOUT == 0 && pl.kernel == 6) {   // 4-step vectors per lane
     if (kp.L % 4 == 0) return launch_rowgroup_pair<IO, 8, true>(kp, st);
     return launch_rowgroup_pair<IO, 8, false>(kp, st);
-  }
-  if (LAYOUT == 0 && pl.kernel == 4) {
-    if (pl.ps == 2) {
-      if (kp.L % 4 == 0) return launch_rowgroup_split<IO, true, 2>(kp, st);
-      return launch_rowgroup_split<IO, false, 2>(kp, st);
-    }
-    if (kp.L % 8 == 0) return launch_rowgroup_split<IO, true, 4>(kp, st);
-    return launch_rowgroup_split<IO, false, 4>(kp, st);
-  }
-  if (LAYOUT == 0 && pl.kernel == 3) {
-    if (kp.L % 4 == 0) return launch_rowgroup_mixed<IO, true>(kp, st);
-    return launch_rowgroup_mixed<IO, false>(kp, st);
   }
   if (LAYOUT == 0 && pl.kernel == 1) {
     if (pl.Npad == 16) return launch_rowgroup<IO, 2>(pl, kp, st);

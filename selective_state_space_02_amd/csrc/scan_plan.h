@@ -18,8 +18,6 @@ namespace ssm {
 struct Plan {
   int kernel = 0;            // 0: workgroup kernel (64 rows, states over waves); 1: row-group kernel;
                              // 2: chunked multi-head kernel on MFMA (ssd_kernels.hip);
-                             // 3: row-group kernel, mixed launch (16 states, 80 channels per workgroup);
-                             // 4: row-group kernel, split launch (16 states, 80 channels per workgroup);
                              // 5 / 6: row-group kernel, two-kind launch (16 states, 80 / 48 channels
                              // per workgroup)
   int ps = 0;                // kernel 2: positions per workgroup
@@ -55,7 +53,6 @@ struct KParams {
   float* wsH;   // [seg][b][n][d] zero-start end state of each aggregated segment ([seg][b][h]
                 //   [slice][state tile][lane][4] in the chunked multi-head kernel)
   float* bct;   // row-group kernel: [b][g][block] B/C tiles in LDS order (bc_tile_kernel)
-  float* bct2;  // split launch: the same tiles per state pair, [b][g][block][pair][t][B C B C]
   const float* conv_w;     // optional input stage (row-group kernels): (dim, conv_k) filters
   const float* conv_b;     // (dim) or NULL
   const float* conv_sin;   // (batch, dim, conv_k-1) raw inputs before t = 0, or NULL (zeros)
@@ -66,7 +63,7 @@ struct KParams {
   int batch, dim, N, Npad, H, P, G;
   int rows_per_group;    // BDL: dim / G;  BLHP: P
   int blocks_per_group;  // row blocks per group / head (64 rows; 8 for the row-group kernel; 80 or 48 for
-                         // the two-kind launches, 80 for the mixed and split ones)
+                         // the two-kind launches)
   int heads_per_group;   // BLHP: H / G
   int softplus;
   int has_z;
@@ -96,8 +93,7 @@ struct UParams {
 };
 
 // Validates dims (no HIP call) and fills the plan; returns SSM_OK or an error code.
-// conv: the plan of a call with the fused input stage (every launch but the split one).
-int make_plan(const ssm_dims_t* d, Plan* plan, bool conv = false);
+int make_plan(const ssm_dims_t* d, Plan* plan);
 
 // Enqueue the kernels of a validated plan.  Returns a hipError_t value (0 = success).
 // scan_kernels.hip is compiled once per discretization; launch_plan picks the build.

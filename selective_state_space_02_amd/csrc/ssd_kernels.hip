@@ -63,12 +63,14 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
   lo = pack_bf(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
-// softplus(r) = max(r, 0) + ln 2 * log2(1 + 2^(-|r| log2 e)); 1 + e in [1, 2] never overflows.
-// Rounding 1 + e costs a relative error of about 2^-24 / dt in small steps, far below the
-// 2^-9 rounding of the bfloat16 inputs this kernel reads.
+// softplus(r) = max(r, 0) + log1p(e), e = 2^(-|r| log2 e), with log1p(e) taken as
+// ln 2 * log2(w) + (e - (w - 1)), w = fl(1 + e) in [1, 2] (never overflows; w - 1 is exact).
+// The second term puts back the rounding of 1 + e, which would otherwise be a relative error
+// of up to 2^-24 / dt in every small step.
 __device__ __forceinline__ float softplus_s(float r) {
   const float e = __builtin_amdgcn_exp2f(-fabsf(r) * kLog2e);
-  return fmaf(__builtin_amdgcn_logf(1.0f + e), kLn2, r > 0.0f ? r : 0.0f);
+  const float w = 1.0f + e;
+  return fmaf(__builtin_amdgcn_logf(w), kLn2, (r > 0.0f ? r : 0.0f) + (e - (w - 1.0f)));
 }
 
 __device__ __forceinline__ float silu_s(float z) {

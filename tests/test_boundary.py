@@ -240,7 +240,7 @@ def test_ssd_override_env(monkeypatch):
 
 def test_mixed_launch_override_env(monkeypatch):
     """SSM_SCAN_MIXED forces the 16-state launch shape (0 plain, 1 80 channels, 48 channels);
-    SSM_SCAN_MIXED4=0 and SSM_SCAN_SPLIT=4/2 select the other 80-channel launches."""
+    the workspace size follows the launch the plan picks."""
     d = dims(batch=4, seqlen=2048, dim=5120, dstate=16)
     ws = scan.workspace_size(d)
     monkeypatch.setenv("SSM_SCAN_MIXED", "0")
@@ -250,25 +250,16 @@ def test_mixed_launch_override_env(monkeypatch):
     monkeypatch.setenv("SSM_SCAN_MIXED", "1")
     d2 = dims(batch=8, seqlen=2048, dim=1536, dstate=16)
     assert "kernel=rowgroup_mixed4" in scan.describe(d2) and "grid=(20,8,1)" in scan.describe(d2)
-    monkeypatch.setenv("SSM_SCAN_MIXED4", "0")
-    assert "kernel=rowgroup_mixed " in scan.describe(d2)
-    monkeypatch.setenv("SSM_SCAN_SPLIT", "2")
-    assert "kernel=rowgroup_split" in scan.describe(d2) and "states_per_wave=2" in scan.describe(d2)
-    monkeypatch.setenv("SSM_SCAN_SPLIT", "4")
-    assert "kernel=rowgroup_split" in scan.describe(d2) and "states_per_wave=4" in scan.describe(d2)
-    assert scan.workspace_size(d) == 2 * ws                             # two tile layouts
-    d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)            # the split launch: one segment
-    assert "kernel=rowgroup_split" in scan.describe(d4) and "grid=(32,1,1)" in scan.describe(d4)
-    monkeypatch.setenv("SSM_SCAN_SEGMENTS", "3")                      # forced segments: not the split launch
-    assert "kernel=rowgroup " in scan.describe(d4) and "grid=(80,1,3)" in scan.describe(d4)
-    monkeypatch.setenv("SSM_SCAN_SPLIT", "0")
-    monkeypatch.setenv("SSM_SCAN_MIXED4", "1")
+    d4 = dims(batch=1, seqlen=131072, dim=2560, dstate=16)
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", "3")
     assert "kernel=rowgroup_mixed4" in scan.describe(d4) and "grid=(32,1,3)" in scan.describe(d4)
+    monkeypatch.setenv("SSM_SCAN_MIXED", "0")
+    assert "kernel=rowgroup " in scan.describe(d4) and "grid=(80,1,3)" in scan.describe(d4)
 
 
 def test_plan_segments_and_launch_choices(monkeypatch):
     """Launch and segment choices of the plan for a few shapes (host logic only)."""
-    for k in ("SSM_SCAN_MIXED", "SSM_SCAN_MIXED4", "SSM_SCAN_SPLIT", "SSM_SCAN_SEGMENTS", "SSM_SCAN_SSD", "SSM_SSD_PS"):
+    for k in ("SSM_SCAN_MIXED", "SSM_SCAN_SEGMENTS", "SSM_SCAN_SSD", "SSM_SSD_PS"):
         monkeypatch.delenv(k, raising=False)
     # the 48-channel launch keeps one segment unless segments are forced
     d = dims(batch=16, seqlen=2048, dim=768, dstate=16)

@@ -91,8 +91,7 @@ def test_conv_scan(name, kw, K, with_state, segs, disc, monkeypatch):
     np.testing.assert_array_equal(cs.double().cpu().numpy(), cs_ref)
 
 
-LAUNCHES = {"plain": {"SSM_SCAN_MIXED": "0"}, "mixed4": {"SSM_SCAN_MIXED": "1"},
-            "mixed": {"SSM_SCAN_MIXED": "1", "SSM_SCAN_MIXED4": "0"}, "mixed48": {"SSM_SCAN_MIXED": "48"}}
+LAUNCHES = {"plain": {"SSM_SCAN_MIXED": "0"}, "mixed4": {"SSM_SCAN_MIXED": "1"}, "mixed48": {"SSM_SCAN_MIXED": "48"}}
 LAUNCH_CASES = [
     ("bf16-K4", dict(io_dtype="bf16", batch=2, seqlen=320, dim=136, dstate=16), 4, True, None),
     ("f32-K3-ragged", dict(io_dtype="f32", batch=2, seqlen=97, dim=90, dstate=16), 3, True, None),

@@ -219,10 +219,7 @@ def test_continuation_matches_single_call():
 
 # ------------------------------------------------------------------ launch shapes for 16 states
 
-LAUNCH16 = {"split4": ({"SSM_SCAN_SPLIT": "4"}, "kernel=rowgroup_split", "states_per_wave=4"),
-            "split2": ({"SSM_SCAN_SPLIT": "2"}, "kernel=rowgroup_split", "states_per_wave=2"),
-            "mixed4": ({}, "kernel=rowgroup_mixed4", ""),
-            "mixed": ({"SSM_SCAN_MIXED4": "0"}, "kernel=rowgroup_mixed ", ""),
+LAUNCH16 = {"mixed4": ({}, "kernel=rowgroup_mixed4", ""),
             "mixed48": ({"SSM_SCAN_MIXED": "48"}, "kernel=rowgroup_mixed48", "")}
 
 
@@ -231,10 +228,9 @@ LAUNCH16 = {"split4": ({"SSM_SCAN_SPLIT": "4"}, "kernel=rowgroup_split", "states
                                    (240, 1, 1), (200, 130, 2), (160, 96, 2), (90, 36, 1), (64, 2052, 1)])
 @pytest.mark.parametrize("launch", list(LAUNCH16))
 def test_mixed_launch(io, D, L, G, launch, monkeypatch):
-    """The 80-channel launches against the oracle: split (states over waves, one channel per
-    lane, 4 or 2 states per wave, plus 16-lane waves) and mixed (8-lane and 16-lane channel
-    waves); partial workgroups, channel counts not a multiple of 4 or 8, one step, lengths
-    not a multiple of 4 or 8, groups."""
+    """The two-kind launches against the oracle (80 channels: 4-lane and 16-lane channel waves;
+    48 channels: 8-lane and 16-lane): partial workgroups, channel counts not a multiple of 4 or
+    8, one step, lengths not a multiple of 4 or 8, groups."""
     env, kname, extra = LAUNCH16[launch]
     monkeypatch.setenv("SSM_SCAN_MIXED", "1")
     for k, v in env.items():
@@ -247,7 +243,7 @@ def test_mixed_launch(io, D, L, G, launch, monkeypatch):
     check_case(c)
 
 
-@pytest.mark.parametrize("launch", ["mixed4", "mixed", "mixed48"])
+@pytest.mark.parametrize("launch", ["mixed4", "mixed48"])
 @pytest.mark.parametrize("L,nseg", [(1000, "3"), (97, "3"), (4100, "5")])
 def test_mixed_launch_segments(L, nseg, launch, monkeypatch):
     """The 80-channel launches over time segments: an aggregate pass per segment before the
@@ -284,28 +280,19 @@ def test_mixed_and_plain_agree():
     readout sum over states differs."""
     c = make_case("mix_vs_plain", layout="bdl", io_dtype="bf16", batch=2, seqlen=512, dim=320, dstate=16,
                   seed=12, has_h0=True, A_kind="lognormal")
-    saved = {k: os.environ.get(k) for k in ("SSM_SCAN_MIXED", "SSM_SCAN_SPLIT", "SSM_SCAN_MIXED4")}
+    saved = os.environ.get("SSM_SCAN_MIXED")
     try:
         os.environ["SSM_SCAN_MIXED"] = "1"
-        os.environ["SSM_SCAN_SPLIT"] = "4"
-        y3, h3 = gpu_run(c)
-        os.environ["SSM_SCAN_SPLIT"] = "2"
-        y2, h2 = gpu_run(c)
-        os.environ["SSM_SCAN_SPLIT"] = "0"
-        os.environ["SSM_SCAN_MIXED4"] = "0"
-        y1, h1 = gpu_run(c)
-        os.environ["SSM_SCAN_MIXED4"] = "1"
         y4, h4 = gpu_run(c)
         os.environ["SSM_SCAN_MIXED"] = "48"
         y5, h5 = gpu_run(c)
         os.environ["SSM_SCAN_MIXED"] = "0"
         y0, h0 = gpu_run(c)
     finally:
-        for k, v in saved.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
-    for y, h in ((y1, h1), (y2, h2), (y3, h3), (y4, h4), (y5, h5)):
+        if saved is None:
+            os.environ.pop("SSM_SCAN_MIXED", None)
+        else:
+            os.environ["SSM_SCAN_MIXED"] = saved
+    for y, h in ((y4, h4), (y5, h5)):
         torch.testing.assert_close(y.float(), y0.float(), rtol=1e-2, atol=1e-2)
         torch.testing.assert_close(h, h0, rtol=1e-5, atol=1e-5)

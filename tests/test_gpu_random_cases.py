@@ -23,7 +23,7 @@ from selective_state_space_02_amd.inputs import make_case
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-ENV_KEYS = ("SSM_SCAN_MIXED", "SSM_SCAN_MIXED4", "SSM_SCAN_SPLIT", "SSM_SCAN_SSD", "SSM_SSD_PS", "SSM_SCAN_SEGMENTS")
+ENV_KEYS = ("SSM_SCAN_MIXED", "SSM_SCAN_SSD", "SSM_SSD_PS", "SSM_SCAN_SEGMENTS")
 
 
 def np_io(t, io):
@@ -54,10 +54,6 @@ def draw(rng, big):
         if N <= 32 and rng.random() < 0.3:
             conv = rng.choice([1, 2, 3, 4])
         env["SSM_SCAN_MIXED"] = rng.choice(["", "0", "1", "48"])
-        if rng.random() < 0.3:
-            env["SSM_SCAN_MIXED4"] = "0"
-        if rng.random() < 0.15 and not conv:
-            env["SSM_SCAN_SPLIT"] = rng.choice(["2", "4"])
     else:
         N = rng.choice([32, 64, 128, 16, 48, 256, 1])
         G = rng.choice([1, 2])

@@ -488,6 +488,50 @@ def test_multihead_layout_equivalence(io):
 
 
 # ---------------------------------------------------------------------------
+# Groups: channels (heads) of group g read B, C of group g only.  A run with G
+# groups equals G runs with one group each on the group's slice of channels
+# (heads) and its own B, C, bit for bit, in both oracle implementations.  This
+# checks the channel -> group mapping of both layouts against slicing, not
+# against the same formula written twice.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("impl", ["c", "numpy"])
+@pytest.mark.parametrize("layout,io,G", [("bdl", "bf16", 2), ("bdl", "f32", 4), ("blhp", "bf16", 2),
+                                         ("blhp", "f32", 3)])
+def test_groups_equal_per_group_runs(layout, io, G, impl):
+    if layout == "bdl":
+        c = make_case(layout="bdl", io_dtype=io, batch=2, seqlen=45, dim=4 * G, dstate=6, ngroups=G, seed=70 + G,
+                      has_h0=True, A_kind="lognormal")
+    else:
+        c = make_case(layout="blhp", io_dtype=io, batch=2, seqlen=45, dim=2 * G * 3, dstate=6, nheads=2 * G,
+                      headdim=3, ngroups=G, seed=80 + G, has_h0=True)
+    y, h = run_case(c, impl=impl)
+    T = c.tensors
+    fn = oracle.scan_f64 if impl == "c" else oracle.scan_numpy_f64
+    D = c.dim
+    for g in range(G):
+        if layout == "bdl":
+            ch = slice(g * D // G, (g + 1) * D // G)
+            part = fn(np_io(T["u"][:, ch], io), np_io(T["delta"][:, ch], io), T["A"][ch].contiguous().numpy(),
+                      np_io(T["B"][:, g:g + 1], io), np_io(T["C"][:, g:g + 1], io), T["D"][ch].contiguous().numpy(),
+                      np_io(T["z"][:, ch], io), T["delta_bias"][ch].contiguous().numpy(), True,
+                      T["h0"][:, ch].contiguous().numpy(), io_dtype=io, ngroups=1)
+            np.testing.assert_array_equal(part[0], y[:, ch])
+            np.testing.assert_array_equal(part[1], h[:, ch])
+        else:
+            hpg = c.nheads // G
+            hs = slice(g * hpg, (g + 1) * hpg)
+            ch = slice(g * hpg * c.headdim, (g + 1) * hpg * c.headdim)
+            part = fn(np_io(T["u"][:, :, hs], io), np_io(T["delta"][:, :, hs], io), T["A"][hs].contiguous().numpy(),
+                      np_io(T["B"][:, :, g:g + 1], io), np_io(T["C"][:, :, g:g + 1], io),
+                      T["D"][ch].contiguous().numpy(), np_io(T["z"][:, :, hs], io),
+                      T["delta_bias"][hs].contiguous().numpy(), True, T["h0"][:, ch].contiguous().numpy(),
+                      layout="blhp", io_dtype=io, ngroups=1)
+            np.testing.assert_array_equal(part[0], y[:, :, hs])
+            np.testing.assert_array_equal(part[1], h[:, ch])
+
+
+# ---------------------------------------------------------------------------
 # The two oracle implementations agree on random cases (both layouts, groups,
 # both storage types), and time-selected output matches the full output.
 # ---------------------------------------------------------------------------
