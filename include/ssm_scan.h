@@ -88,6 +88,7 @@ extern "C" {
 #define SSM_ERR_ALIAS -5       /* y or h_last overlaps an input or each other */
 #define SSM_ERR_WORKSPACE -6   /* caller workspace smaller than ssm_scan_workspace_size */
 #define SSM_ERR_HIP -7         /* a HIP runtime call failed (see ssm_strerror) */
+#define SSM_ERR_SCRATCH -8     /* ssm_scan_fwd_noalloc: the launch needs more than the static scratch */
 
 typedef struct ssm_dims {
   int64_t batch;     /* B >= 1 */
@@ -165,6 +166,27 @@ typedef struct ssm_conv {
 int ssm_conv_scan_fwd(const void* x, const ssm_conv_t* conv, const void* delta, const float* A, const void* B,
                       const void* C, const float* D, const void* z, const float* delta_bias, int softplus_flag,
                       const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream);
+
+/*
+ * Allocation-free variant of ssm_scan_fwd, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, layouts, validation, stream semantics and errors are those of ssm_scan_fwd,
+ * except that dims->workspace and dims->workspace_bytes are ignored: the scratch comes from
+ * a static device array of ssm_scan_scratch_capacity() bytes (32 MiB) that the library holds
+ * on every GPU it runs on until the process ends.  The call makes no hipMalloc/hipFree, no
+ * stream-ordered allocation and no other allocating call.  A launch that needs more scratch
+ * than the array holds (ssm_scan_workspace_size(dims) > ssm_scan_scratch_capacity()) returns
+ * SSM_ERR_SCRATCH before any HIP call.  On its first call on a device (with that device
+ * current) it looks the array's device address up; a failure there returns SSM_ERR_HIP.
+ * All calls on one GPU share that GPU's array, so calls that overlap in time on one GPU
+ * (other streams, other host threads) race on it and must be serialised by the caller.
+ */
+int ssm_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                         const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream);
+
+/* Bytes of the static device scratch ssm_scan_fwd_noalloc uses (per GPU). */
+size_t ssm_scan_scratch_capacity(void);
 
 /* Bytes of scratch ssm_scan_fwd needs for these dims (0 if none); 0 also for invalid dims. */
 size_t ssm_scan_workspace_size(const ssm_dims_t* dims);

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssm_scan.so")
 SOURCES = [os.path.join(CSRC, "scan_api.cpp"), os.path.join(CSRC, "scan_kernels.hip"),
-           os.path.join(CSRC, "update_kernels.hip"), os.path.join(CSRC, "ssd_kernels.hip")]
+           os.path.join(CSRC, "update_kernels.hip"), os.path.join(CSRC, "ssd_kernels.hip"),
+           os.path.join(CSRC, "scratch.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -68,6 +69,7 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
+
 
 
 if __name__ == "__main__":

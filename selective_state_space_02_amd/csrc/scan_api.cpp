@@ -266,6 +266,9 @@ const char* ssm_strerror(int code) {
     case SSM_ERR_ALIAS: return "an output overlaps an input or the other output";
     case SSM_ERR_WORKSPACE: return "workspace is smaller than ssm_scan_workspace_size()";
     case SSM_ERR_HIP: return ssm::g_hip_msg[0] ? ssm::g_hip_msg : "HIP runtime error";
+    case SSM_ERR_SCRATCH:
+      return "the launch needs more scratch than the static device scratch of ssm_scan_fwd_noalloc holds "
+             "(ssm_scan_scratch_capacity() bytes)";
     default: return "unknown error code";
   }
 }
@@ -297,9 +300,12 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
   return SSM_OK;
 }
 
+// use_scratch: the allocation-free variant (the library's static device scratch replaces the
+// workspace; no allocation of any kind).
 static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, const float* A, const void* B,
                       const void* C, const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                      const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream) {
+                      const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream,
+                      bool use_scratch = false) {
   ssm::g_hip_msg[0] = 0;
   if (!u || !delta || !A || !B || !C || !y || !dims) return SSM_ERR_NULL_ARG;
   ssm::Plan pl;
@@ -356,9 +362,14 @@ static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, 
     }
   }
 
-  void* ws = dims->workspace;
+  void* ws = use_scratch ? nullptr : dims->workspace;
   bool own_ws = false;
-  if (pl.ws_bytes) {
+  if (use_scratch && pl.ws_bytes) {
+    if (pl.ws_bytes > ssm::scratch_capacity()) return SSM_ERR_SCRATCH;
+    const int rs = ssm::scratch_address(&ws, ssm::g_hip_msg, sizeof ssm::g_hip_msg);
+    if (rs != SSM_OK) return rs;
+  }
+  if (pl.ws_bytes && !use_scratch) {
     if (ws) {
       if (dims->workspace_bytes < pl.ws_bytes) return SSM_ERR_WORKSPACE;
       if (ssm::misaligned(ws)) return SSM_ERR_ALIGN;
@@ -424,6 +435,14 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                  const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream) {
   return scan_entry(u, nullptr, delta, A, B, C, D, z, delta_bias, softplus_flag, h0, y, h_last, dims, stream);
 }
+
+int ssm_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                         const float* h0, void* y, float* h_last, const ssm_dims_t* dims, void* stream) {
+  return scan_entry(u, nullptr, delta, A, B, C, D, z, delta_bias, softplus_flag, h0, y, h_last, dims, stream, true);
+}
+
+size_t ssm_scan_scratch_capacity(void) { return ssm::scratch_capacity(); }
 
 int ssm_conv_scan_fwd(const void* x, const ssm_conv_t* conv, const void* delta, const float* A, const void* B,
                       const void* C, const float* D, const void* z, const float* delta_bias, int softplus_flag,

@@ -107,4 +107,10 @@ int launch_ssd(const KParams& kp, int ps, int zoh, void* stream);
 // Enqueue the state-update kernel.  Returns a hipError_t value (0 = success).
 int launch_update(const UParams& p, int layout, int io, int Npad, void* stream);
 
+// The static device scratch of the allocation-free entry point (scratch.hip): its size in
+// bytes, and its device address on the current device (looked up once per device).
+// scratch_address returns SSM_OK or SSM_ERR_HIP (with a message in msg).
+size_t scratch_capacity();
+int scratch_address(void** out, char* msg, size_t msg_len);
+
 }  // namespace ssm

@@ -33,9 +33,10 @@ SSM_ERR_ALIGN = -4
 SSM_ERR_ALIAS = -5
 SSM_ERR_WORKSPACE = -6
 SSM_ERR_HIP = -7
+SSM_ERR_SCRATCH = -8
 
 EXPORTED = ("ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_strerror", "ssm_scan_describe", "ssm_scan_version",
-            "ssm_state_update", "ssm_conv_scan_fwd")
+            "ssm_state_update", "ssm_conv_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_scratch_capacity")
 
 
 class Dims(ctypes.Structure):
@@ -96,6 +97,11 @@ def load_library():
         lib.ssm_conv_scan_fwd.restype = ctypes.c_int
         lib.ssm_conv_scan_fwd.argtypes = [vp, ctypes.POINTER(Conv), vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
                                           vp, vp, ctypes.POINTER(Dims), vp]
+        lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
+        lib.ssm_scan_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                             ctypes.POINTER(Dims), vp]
+        lib.ssm_scan_scratch_capacity.restype = ctypes.c_size_t
+        lib.ssm_scan_scratch_capacity.argtypes = []
         lib.ssm_state_update.restype = ctypes.c_int
         lib.ssm_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                          ctypes.POINTER(Dims), vp]
@@ -130,6 +136,18 @@ def call_raw(u, delta, A, B, C, D, z, delta_bias, softplus, h0, y, h_last, dims:
     """Direct ABI call with integer addresses (None = NULL).  Returns the status code."""
     return int(load_library().ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, int(bool(softplus)), h0, y,
                                           h_last, ctypes.byref(dims), stream))
+
+
+def call_noalloc_raw(u, delta, A, B, C, D, z, delta_bias, softplus, h0, y, h_last, dims: Dims, stream=None) -> int:
+    """Direct ABI call of ssm_scan_fwd_noalloc (the library's static device scratch, no
+    allocation) with integer addresses (None = NULL).  Returns the status code."""
+    return int(load_library().ssm_scan_fwd_noalloc(u, delta, A, B, C, D, z, delta_bias, int(bool(softplus)), h0, y,
+                                                  h_last, ctypes.byref(dims), stream))
+
+
+def scratch_capacity() -> int:
+    """Bytes of the static device scratch ssm_scan_fwd_noalloc uses on each GPU."""
+    return int(load_library().ssm_scan_scratch_capacity())
 
 
 def _ptr(t: Optional[torch.Tensor]):

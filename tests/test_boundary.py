@@ -327,3 +327,20 @@ def test_header_is_plain_c_and_a_c_program_links(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.startswith("ok"), (r.returncode, r.stdout, r.stderr)
+
+
+def test_noalloc_rejects_beyond_scratch_before_any_hip_call():
+    """ssm_scan_fwd_noalloc validates like ssm_scan_fwd, then refuses a launch whose scratch
+    exceeds the static device array, all before any HIP call (fake addresses here)."""
+    cap = scan.scratch_capacity()
+    assert cap == 32 << 20
+    big = dims(batch=64, seqlen=131072, dim=16, dstate=16)
+    assert scan.workspace_size(big) > cap
+    a = dict(P)
+    args = (a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], True, a["h0"], a["y"], a["h_last"])
+    assert scan.call_noalloc_raw(*args, big) == scan.SSM_ERR_SCRATCH
+    assert "static device scratch" in scan.strerror(scan.SSM_ERR_SCRATCH)
+    # the ordinary argument checks come first
+    assert scan.call_noalloc_raw(*args, dims(dim=0)) == scan.SSM_ERR_BAD_DIMS
+    assert scan.call_noalloc_raw(None, *args[1:], dims()) == scan.SSM_ERR_NULL_ARG
+    assert scan.call_noalloc_raw(*args[:9], a["u"] + 8, *args[10:], dims()) == scan.SSM_ERR_ALIGN
