@@ -26,39 +26,66 @@ sys.path.insert(0, ROOT)
 METRIC = "selective-scan elements/s (B·L·D·N) + achieved HBM GB/s vs MI355X peak"
 DEFAULT_WORKLOAD = "mamba2p8b_layer"
 
-# MI355X figures used for the rooflines: vendor peaks; 32 fp32 lanes per SIMD per clock as
-# measured for v_fmac_f32 on gfx950, transcendentals at a quarter of that.
+# MI355X figures used for the rooflines.  Vendor peaks for HBM and the bf16 matrix units.
+# The fp32 vector peak is derived from the unit counts and the boost clock: 256 CUs x 4 SIMDs
+# x 16 fp32 lanes per clock x 2.4 GHz = 39.3 T lane-ops/s (78.6 TFLOP/s with FMA = 2; the
+# published 157.3 TFLOP/s needs packed fp32, which this library does not emit).  A
+# transcendental (v_exp_f32, v_log_f32, v_rcp_f32) retires 8 lanes per clock, i.e. it holds
+# the VALU for two fp32 issue slots, and does not overlap with fp32 work.  Both rates are
+# measured by `bench.py --valu-rates` (profiles/valu_rates_gfx950.txt).
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak
-CUS, SIMDS, LANES_PER_CLK, CLOCK_HZ = 256, 4, 32, 2.4e9
-VALU_SLOT_PEAK = CUS * SIMDS * LANES_PER_CLK * CLOCK_HZ       # 78.64e12 fp32 lane-ops/s (= 157.3 TFLOP/s FMA)
-TRANS_SLOTS = 4                                               # exp2/log2/rcp issue at 1/4 of the fp32 rate
+CUS, SIMDS, CLOCK_HZ = 256, 4, 2.4e9
+FP32_LANES_PER_CLK, TRANS_LANES_PER_CLK = 16, 8
+VALU_SLOT_PEAK = CUS * SIMDS * FP32_LANES_PER_CLK * CLOCK_HZ   # 39.32e12 fp32 lane-ops/s
+TRANS_PEAK = CUS * SIMDS * TRANS_LANES_PER_CLK * CLOCK_HZ      # 19.66e12 transcendentals/s
+TRANS_SLOTS = FP32_LANES_PER_CLK // TRANS_LANES_PER_CLK        # VALU slots one transcendental holds
 
-# Algorithmic work of the path, in fp32 VALU slots.
-#  per (b,d,t,n): exp(dt*A) [1 mul + 1 transcendental], dt*u*B [1 mul], h update [1 fma], readout [1 fma]
-#  per (b,d,t)  : softplus [bias add, 1+e add, exp, log], dt*u [mul], D*u [fma],
-#                 SiLU gate [exp, 1+e add, rcp, z*s mul, y*s mul]
+# Algorithmic work of the path.  "ops" are fp32 VALU instructions per lane, "trans" the
+# transcendentals among them (each counted as TRANS_SLOTS slots in the ALU bound).
+#  per (b,d,t,n): dt*A [mul], exp2 [trans], (dt*u)*B [mul], h update [fma], readout [fma]
+#  per (b,d,t)  : dt = softplus(delta + bias) [add, mul, exp2, add, log2, max, fma],
+#                 dt*u [mul], D*u [fma], SiLU gate [mul, exp2, add, rcp, mul, mul]
 #  multi-head layout: exp(dt*A) is per (b,t,h), so per element only dt*u*B, h update, readout.
-#  exact zero-order hold (--discretization zoh): per (b,d,t,n) in the per-channel layout, x = dt*A [mul],
-#                 expm1 from the exp [add], divide by x [rcp + mul], scale B̄ [mul]; per (b,t,h) in the
-#                 multi-head layout (the factor is per head).
-ZOH_SLOTS = 4 + TRANS_SLOTS
-#  fused input stage (--conv K): per (b,d,t) K fma for the causal conv, SiLU [exp, 1+e add, rcp, mul].
-def conv_slots(K):
-    return K + 2 + 2 * TRANS_SLOTS if K else 0
+#  exact zero-order hold: per element x = dt*A [mul], expm1 = a - 1 [add], 1/x [rcp],
+#                 (a-1)/x [mul], scale the input [mul]; per (b,t,h) in the multi-head layout.
+#  fused input stage of width K: per (b,d,t) K fma for the causal conv, SiLU [mul, exp2, add, rcp, mul].
+ELEM_OPS, ELEM_TRANS = 5, 1
+SOFTPLUS_OPS, SOFTPLUS_TRANS = 7, 2
+GATE_OPS, GATE_TRANS = 6, 2
+ZOH_OPS, ZOH_TRANS = 5, 1
 
 
-def algorithmic_slots(case, zoh=False, conv_k=0) -> float:
+def conv_ops(K):
+    return (K + 5, 2) if K else (0, 0)
+
+
+def algorithmic_ops(case, zoh=False, conv_k=0):
+    """(fp32 VALU ops, transcendentals) per call of the scan as the method defines it."""
     Bsz, L, Dm, N = case.batch, case.seqlen, case.dim, case.dstate
     has_z = case.tensors["z"] is not None
-    per_row_step = (2 + 2 * TRANS_SLOTS) + 2 + ((3 + 2 * TRANS_SLOTS) if has_z else 0) + conv_slots(conv_k)
+    sp = (SOFTPLUS_OPS, SOFTPLUS_TRANS) if case.softplus else (1, 0)          # the bias add alone without softplus
+    gate = (GATE_OPS, GATE_TRANS) if has_z else (0, 0)
+    cv = conv_ops(conv_k)
+    row_ops = sp[0] + 1 + 1 + gate[0] + cv[0]            # + dt*u, D*u
+    row_trans = sp[1] + gate[1] + cv[1]
     if case.layout == "bdl":
-        per_elem = 4 + TRANS_SLOTS + (ZOH_SLOTS if zoh else 0)
-        return Bsz * L * Dm * (N * per_elem + per_row_step)
-    per_elem = 3
-    per_head_step = (2 + 2 * TRANS_SLOTS) + (1 + TRANS_SLOTS) + (ZOH_SLOTS if zoh else 0)
-    per_chan_step = 2 + ((3 + 2 * TRANS_SLOTS) if has_z else 0)
-    return Bsz * L * (Dm * (N * per_elem + per_chan_step) + case.nheads * per_head_step)
+        el_ops = ELEM_OPS + (ZOH_OPS if zoh else 0)
+        el_trans = ELEM_TRANS + (ZOH_TRANS if zoh else 0)
+        rows = Bsz * L * Dm
+        return rows * (N * el_ops + row_ops), rows * (N * el_trans + row_trans)
+    # multi-head: decay per (b,t,h); softplus per (b,t,h); dt*u, D*u, gate per (b,t,d)
+    head_ops = sp[0] + 2 + (ZOH_OPS if zoh else 0)       # + dt*A mul, exp2
+    head_trans = sp[1] + 1 + (ZOH_TRANS if zoh else 0)
+    chan_ops = 2 + gate[0]
+    ops = Bsz * L * (Dm * (N * 3 + chan_ops) + case.nheads * head_ops)
+    trans = Bsz * L * (Dm * gate[1] + case.nheads * head_trans)
+    return ops, trans
+
+
+def valu_slots(ops, trans):
+    """fp32 VALU issue slots: every op one slot, a transcendental TRANS_SLOTS."""
+    return ops + (TRANS_SLOTS - 1) * trans
 
 
 def ssd_form_flops(case, chunk: int = 64) -> float:
@@ -118,6 +145,16 @@ def load_traffic(workload: str, variant: str = ""):
     if rec.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def host_cpus():
+    """The host's CPU counts beside the threads the oracle ran on: the oracle uses every core
+    this process may run on, up to the 16 a one-GPU machine grants each GPU."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"host_cpu_count": os.cpu_count(), "usable_cpus": usable, "cpu_share_per_gpu": 16}
 
 
 def cpu_baseline(case, budget_s: float = 12.0, zoh: bool = False, conv=None):
@@ -185,7 +222,7 @@ def cpu_baseline(case, budget_s: float = 12.0, zoh: bool = False, conv=None):
     if case.layout == "blhp":
         nch1 = max(case.headdim, (nch1 // case.headdim) * case.headdim)
     dt1, el1, _ = run(1, min(nch1, case.dim), threads=1)
-    return {"value": el / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+    return {"value": el / dt, "unit": "elements/s", "cores": threads, "kind": "oracle", **host_cpus(),
             "sample": f"{what}, all {case.seqlen} steps, {case.dstate} states: {el:.3e} elements in {dt:.2f} s",
             "value_1thread": el1 / dt1,
             "sample_1thread": f"batch item 0, first {min(nch1, case.dim)} channels, 1 thread: {el1:.3e} elements in "
@@ -243,7 +280,7 @@ def cpu_baseline_decode(case, budget_s: float = 12.0):
         if dt > budget_s or reps >= 200:
             break
     el = reps * case.elements
-    return {"value": el / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+    return {"value": el / dt, "unit": "elements/s", "cores": threads, "kind": "oracle", **host_cpus(),
             "sample": f"{reps} full one-step updates of the whole batch ({case.elements:.3e} elements each) "
                       f"in {dt:.2f} s"}
 
@@ -303,6 +340,38 @@ def bench_decode(args, case, dev):
     print(json.dumps(line), flush=True)
 
 
+def valu_rates():
+    """Issue rates behind the ALU and transcendental bounds: each kind of instruction alone on
+    8 independent chains per lane, at 1 to 8 waves per SIMD, plus the scan's own element mix
+    and 4 fma + 1 exp (to show that a transcendental and fp32 work add up); HBM read and copy."""
+    import ctypes
+
+    from selective_state_space_02_amd import build as hipbuild
+
+    if not os.path.exists(hipbuild.RATES_LIB):
+        raise RuntimeError(f"{hipbuild.RATES_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(hipbuild.RATES_LIB)
+    lib.ssm_rates_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.ssm_rates_hbm.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    kinds = {0: "v_fma_f32", 1: "v_mul_f32", 2: "v_exp_f32", 3: "v_log_f32", 4: "v_rcp_f32",
+             5: "scan element (mul, exp2, mul, fma, fma)", 6: "4 fma + 1 exp2"}
+    for k, name in kinds.items():
+        for w in (1, 2, 4, 8):
+            res = (ctypes.c_double * 4)()
+            rc = lib.ssm_rates_run(k, w, res)
+            if rc != 0:
+                raise RuntimeError(f"ssm_rates_run({k}, {w}) failed: hipError {rc}")
+            ms, ghz, per_s, cyc = list(res)
+            print(json.dumps({"rate": name, "waves_per_simd": w, "ms": round(ms, 4), "clock_GHz": round(ghz, 3),
+                              "units_per_s_per_simd": per_s, "cycles_per_unit_per_simd": round(cyc, 3),
+                              "lanes_per_clk": round(64 / cyc, 2)}), flush=True)
+    res = (ctypes.c_double * 2)()
+    rc = lib.ssm_rates_hbm(1024, res)
+    if rc != 0:
+        raise RuntimeError(f"ssm_rates_hbm failed: hipError {rc}")
+    print(json.dumps({"rate": "HBM 1 GiB", "read_GBs": round(res[0], 1), "copy_GBs": round(res[1], 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +387,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run only a plain copy of this many MiB (counter calibration), then exit")
+    ap.add_argument("--valu-rates", action="store_true",
+                    help="measure the fp32 / transcendental issue rates, clock and HBM stream rates the "
+                         "rooflines rest on (libssm_rates.so), print one JSON line per measurement, then exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -332,6 +404,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.valu_rates:
+        return valu_rates()
 
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
@@ -398,13 +473,44 @@ def main():
     elements = case.elements
     value = elements / (ms_per_step * 1e-3)
 
-    slots = algorithmic_slots(case, zoh=args.discretization == "zoh", conv_k=args.conv)
-    achieved = slots / (launch_ms * 1e-3) / 1e12
-    peak = VALU_SLOT_PEAK / 1e12
+    ops, trans = algorithmic_ops(case, zoh=args.discretization == "zoh", conv_k=args.conv)
+    slots = valu_slots(ops, trans)
     abytes = algorithmic_bytes(case) + (case.dim * (args.conv + 1) * 4 if args.conv else 0)
     variant = ("_zoh" if args.discretization == "zoh" else "") + (f"_conv{args.conv}" if args.conv else "")
     traffic = load_traffic(args.workload, variant)
-    hbm_gbs = abytes / (launch_ms * 1e-3) / 1e9
+    kernel_s = launch_ms * 1e-3
+    hbm_gbs = abytes / kernel_s / 1e9
+    hbm = {"bound": "hbm", "achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": hbm_gbs / HBM_PEAK_GBS,
+           "traffic": traffic, "algorithmic_bytes_per_launch": abytes}
+    alu = {"bound": "alu", "achieved": slots / kernel_s / 1e12, "peak": VALU_SLOT_PEAK / 1e12, "unit": "TOP/s",
+           "frac": slots / kernel_s / VALU_SLOT_PEAK, "algorithmic_ops_per_launch": slots,
+           "op": f"fp32 VALU lane-issue slot (fma/mul/add = 1, transcendental = {TRANS_SLOTS}); peak = 256 CUs x 4 "
+                 f"SIMDs x {FP32_LANES_PER_CLK} fp32 lanes/clk x 2.4 GHz"}
+    trn = {"bound": "trans", "achieved": trans / kernel_s / 1e12, "peak": TRANS_PEAK / 1e12, "unit": "T/s",
+           "frac": trans / kernel_s / TRANS_PEAK, "transcendentals_per_launch": trans,
+           "op": f"v_exp_f32 / v_log_f32 / v_rcp_f32; peak = 256 CUs x 4 SIMDs x {TRANS_LANES_PER_CLK} lanes/clk x 2.4 GHz"}
+    ssd = "kernel=ssd" in plan
+    if ssd:
+        # the chunked form regroups the recurrence onto bf16 MFMA: the scan-form VALU count is not
+        # work this kernel issues, so the line reports HBM with the matrix units beside it
+        flops = ssd_form_flops(case)
+        mf = flops / kernel_s / 1e12
+        roof = hbm
+        extra = {"mfma": {"bound": "mfma", "achieved": mf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": mf / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": flops,
+                          "op": "chunked-form matrix flops, each product counted once (dense bf16 peak)"}}
+        dtype = "bf16"   # matrix operands (hi/lo split); accumulation and the elementwise work in fp32
+    else:
+        # one lane per (channel, state) in fp32: bound by VALU issue, with HBM and the
+        # transcendental pipe beside it
+        roof = alu
+        extra = {"hbm": hbm, "trans": trn}
+        dtype = "f32"
+    roof = dict(roof)
+    if roof["bound"] != "hbm":
+        roof["traffic"] = traffic
+    roof.update({"kernel_ms": launch_ms, "kernel_ms_median": per_launch[len(per_launch) // 2],
+                 "kernel_ms_min": per_launch[0]})
 
     line = {
         "metric": METRIC,
@@ -417,25 +523,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "layout": case.layout, "io_dtype": case.io_dtype, "batch": case.batch,
                    "seqlen": case.seqlen, "dim": case.dim, "dstate": case.dstate, "nheads": case.nheads,
                    "headdim": case.headdim, "ngroups": case.ngroups, "discretization": args.discretization,
                    "conv_width": args.conv, "plan": plan},
-        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
-                     "frac": achieved / peak, "traffic": traffic,
-                     "kernel_ms": launch_ms, "kernel_ms_median": per_launch[len(per_launch) // 2],
-                     "kernel_ms_min": per_launch[0], "algorithmic_ops_per_launch": slots,
-                     "op": "fp32 VALU lane-issue slot (transcendental = 4)"},
-        "hbm": {"algorithmic_bytes_per_launch": abytes, "achieved_GBs": hbm_gbs, "peak_GBs": HBM_PEAK_GBS,
-                "frac": hbm_gbs / HBM_PEAK_GBS},
+        "roofline": roof,
+        **extra,
     }
-    if "kernel=ssd" in plan:   # the chunked form runs its contractions on bf16 MFMA
-        mf = ssd_form_flops(case) / (launch_ms * 1e-3) / 1e12
-        line["mfma"] = {"achieved": mf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": mf / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": ssd_form_flops(case),
-                        "op": "chunked-form matrix flops, each product counted once (dense bf16 peak)"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget, zoh=args.discretization == "zoh",
                                             conv=None if conv is None else (conv[0].cpu().numpy(),

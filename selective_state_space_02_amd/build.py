@@ -14,6 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssm_scan.so")
+RATES_LIB = os.path.join(PKG, "libssm_rates.so")
 SOURCES = [os.path.join(CSRC, "scan_api.cpp"), os.path.join(CSRC, "scan_kernels.hip"),
            os.path.join(CSRC, "update_kernels.hip"), os.path.join(CSRC, "ssd_kernels.hip"),
            os.path.join(CSRC, "scratch.hip")]
@@ -68,8 +69,17 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    build_rates(verbose)
     return LIB
 
+
+def build_rates(verbose: bool = False) -> str:
+    """The issue-rate measurements behind the rooflines (bench.py --valu-rates), a library of
+    their own: nothing in the scan library depends on them."""
+    tmp = RATES_LIB + ".tmp"
+    _run([HIPCC, *hipcc_flags(), "-shared", "-o", tmp, os.path.join(CSRC, "valu_rates.hip")], verbose)
+    os.replace(tmp, RATES_LIB)
+    return RATES_LIB
 
 
 if __name__ == "__main__":
