@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libssm_scan.so")
 RATES_LIB = os.path.join(PKG, "libssm_rates.so")
 SOURCES = [os.path.join(CSRC, "scan_api.cpp"), os.path.join(CSRC, "scan_kernels.hip"),
            os.path.join(CSRC, "update_kernels.hip"), os.path.join(CSRC, "ssd_kernels.hip"),
-           os.path.join(CSRC, "scratch.hip"), os.path.join(CSRC, "tscan_kernels.hip")]
+           os.path.join(CSRC, "scratch.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

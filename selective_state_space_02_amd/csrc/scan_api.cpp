@@ -240,19 +240,6 @@ int make_plan(const ssm_dims_t* d, Plan* pl) {
       }
     }
   }
-  // The time-parallel kernel (16 states, B̄ = Δ·B): one channel per wave, time over the
-  // lanes, no time segments.  SSM_SCAN_TSCAN=1 selects it (tests, tuning).
-  if (p.kernel == 1 || p.kernel == 5 || p.kernel == 6) {
-    const char* tenv = std::getenv("SSM_SCAN_TSCAN");
-    if (p.Npad == 16 && d->discretization == SSM_DISC_DELTA_B && tenv && *tenv == '1') {
-      p.kernel = 7;
-      p.nseg = 1;
-      p.seg_len = d->seqlen;
-      p.seg_bytes = 0;
-      p.blocks_per_group = (int)((rows_per_group + 3) / 4);
-      p.grid_rows = (int)(groups_or_heads * p.blocks_per_group);
-    }
-  }
   p.ws_bytes = p.bc_bytes + p.seg_bytes;
   *pl = p;
   return SSM_OK;
@@ -300,8 +287,7 @@ int ssm_scan_describe(const ssm_dims_t* dims, char* buf, size_t buf_len) {
     std::snprintf(buf, buf_len,
                   "kernel=%s layout=%s io=%s disc=%s NS=%d NW=%d TB=%d Npad=%d grid=(%d,%lld,%d) seg_len=%lld vec=%d "
                   "ws=%zu",
-                  p.kernel == 7   ? "tscan"
-                  : p.kernel == 6 ? "rowgroup_mixed48"
+                  p.kernel == 6   ? "rowgroup_mixed48"
                   : p.kernel == 5 ? "rowgroup_mixed4"
                   : p.kernel == 2 ? "ssd"
                   : p.kernel == 1 ? "rowgroup"

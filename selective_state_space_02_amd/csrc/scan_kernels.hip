@@ -1154,13 +1154,6 @@ int launch_rowgroup_pair(const KParams& kp, hipStream_t st) {
 
 template <int LAYOUT, typename IO>
 int launch_io(const Plan& pl, const KParams& kp, hipStream_t st) {
-  if (LAYOUT == 0 && pl.kernel == 7) {   // time-parallel kernel: the B/C tiles, then the scan
-    if (kZOH) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL((bc_tile_kernel<IO, 16>), dim3(kp.nblk, kp.G, kp.batch), dim3(256), 0, st, kp);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return (int)e;
-    return launch_tscan(kp, IO::kBytes == 2, st);
-  }
   if (LAYOUT == 0 && pl.kernel == 5) {   // 8-step vectors per lane
     if (kp.L % 8 == 0) return launch_rowgroup_pair<IO, 4, true>(kp, st);
     return launch_rowgroup_pair<IO, 4, false>(kp, st);

@@ -19,8 +19,7 @@ struct Plan {
   int kernel = 0;            // 0: workgroup kernel (64 rows, states over waves); 1: row-group kernel;
                              // 2: chunked multi-head kernel on MFMA (ssd_kernels.hip);
                              // 5 / 6: row-group kernel, two-kind launch (16 states, 80 / 48 channels
-                             // per workgroup); 7: time-parallel kernel (16 states, one channel per
-                             // wave, time spread over the lanes: tscan_kernels.hip)
+                             // per workgroup)
   int ps = 0;                // kernel 2: positions per workgroup
   int disc = 0;              // SSM_DISC_DELTA_B or SSM_DISC_ZOH
   int layout = 0, io = 0;
@@ -101,9 +100,6 @@ int make_plan(const ssm_dims_t* d, Plan* plan);
 int launch_plan(const Plan& plan, const KParams& kp, void* stream);
 int launch_plan_delta_b(const Plan& plan, const KParams& kp, void* stream);
 int launch_plan_zoh(const Plan& plan, const KParams& kp, void* stream);
-
-// Enqueue the time-parallel kernel (per-channel layout, 16 states, B/C tiles already built).
-int launch_tscan(const KParams& kp, bool bf16, void* stream);
 
 // Enqueue the chunked multi-head kernel (bf16 storage, N in {32,64,128}, ps in {32,64} dividing P).
 int launch_ssd(const KParams& kp, int ps, int zoh, void* stream);

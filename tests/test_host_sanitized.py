@@ -19,7 +19,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "selective_state_space_02_amd")
 OBJS = [os.path.join(PKG, "_build", f) for f in ("scan_kernels_delta_b.o", "scan_kernels_zoh.o", "update_kernels.o",
-                                                 "ssd_kernels.o", "scratch.o", "tscan_kernels.o")]
+                                                 "ssd_kernels.o", "scratch.o")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FUZZ = r'''
