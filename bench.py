@@ -372,6 +372,178 @@ def valu_rates():
     print(json.dumps({"rate": "HBM 1 GiB", "read_GBs": round(res[0], 1), "copy_GBs": round(res[1], 1)}), flush=True)
 
 
+# ---------------------------------------------------------------------------------------------
+# rocprofv3 summaries (profiles/): text tables and the HBM-traffic record load_traffic reads.
+# Input: one directory per workload holding the CSV output (-f csv) of
+#   trace/          rocprofv3 --kernel-trace --stats -o trace -- python3 bench.py <args> --steps 20 --warmup 5 --no-cpu-baseline
+#   pmc_FETCH_SIZE/ rocprofv3 --pmc FETCH_SIZE -o pmc -- python3 bench.py <args> --steps 3 --warmup 1 --rotate 1 --no-cpu-baseline
+#   pmc_WRITE_SIZE/ the same with WRITE_SIZE
+#   sq1/ sq2/ sq3/  (optional) the same with the SQ / GRBM counter sets of SQ_PASSES
+# and a calibration directory with pmc_FETCH_SIZE/ and pmc_WRITE_SIZE/ of
+#   rocprofv3 --pmc <C> -o pmc -- python3 bench.py --calib-copy-mb 512
+SQ_PASSES = [
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_LDS SQ_ACTIVE_INST_LDS "
+    "SQ_WAIT_INST_LDS",
+    "SQ_WAIT_INST_ANY SQ_INSTS_VALU_TRANS_F32 SQ_LDS_BANK_CONFLICT SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES "
+    "SQ_INSTS_SALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR GRBM_GUI_ACTIVE GRBM_COUNT",
+    "SQ_WAIT_ANY SQ_LDS_ADDR_CONFLICT SQ_LDS_UNALIGNED_STALL SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL "
+    "SQ_INSTS_SMEM SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VMEM",
+]
+
+
+def _short_kernel(name: str) -> str:
+    return name.replace("ssm::(anonymous namespace)::", "").replace("(ssm::KParams)", "")
+
+
+def _csv_rows(path: str):
+    import csv
+    import glob
+    hits = sorted(glob.glob(os.path.join(path, "**", "*.csv"), recursive=True))
+    return [(f, list(csv.DictReader(open(f, newline="")))) for f in hits]
+
+
+def _pmc_per_dispatch(path: str):
+    """{kernel: {counter: mean value per dispatch}} from a --pmc run's counter_collection.csv."""
+    acc = {}
+    for f, rows in _csv_rows(path):
+        if not f.endswith("counter_collection.csv"):
+            continue
+        for r in rows:
+            k = r["Kernel_Name"]
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            d = acc.setdefault(k, {})
+            d.setdefault(r["Counter_Name"], {})
+            d[r["Counter_Name"]][key] = d[r["Counter_Name"]].get(key, 0.0) + float(r["Counter_Value"])
+    return {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def profile_summary(args) -> None:
+    """Write profiles/<prefix>_<tag>.txt, pmc_<tag>.json and (with SQ passes) sq_counters_<tag>.txt."""
+    from selective_state_space_02_amd.inputs import DECODE_CONFIGS, make_config
+
+    src, tag = args.profile_summary, args.profile_tag
+    wl_args = f"--workload {args.workload}"
+    if args.discretization != "delta_b":
+        wl_args += f" --discretization {args.discretization}"
+    if args.conv:
+        wl_args += f" --conv {args.conv}"
+    variant = ("_zoh" if args.discretization == "zoh" else "") + (f"_conv{args.conv}" if args.conv else "")
+    decode = args.workload in DECODE_CONFIGS
+    what = "state update" if decode else "selective scan"
+    prefix = "update" if decode else "scan"
+    bench_cmd = "python3 /root/repo/bench.py"
+    cmds = [f"rocprofv3 --kernel-trace --stats -f csv -d <out>/trace -o trace -- {bench_cmd} {wl_args} --steps 20 "
+            f"--warmup 5 --no-cpu-baseline"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmds.append(f"rocprofv3 --pmc {c} -f csv -d <out>/pmc_{c} -o pmc -- {bench_cmd} {wl_args} --steps 3 "
+                    f"--warmup 1 --rotate 1 --no-cpu-baseline")
+    cmds.append(f"rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE -f csv -d <calib>/pmc_<C> -o pmc -- {bench_cmd} "
+                f"--calib-copy-mb 512")
+
+    # kernel trace
+    stats = []
+    for f, rows in _csv_rows(os.path.join(src, "trace")):
+        if f.endswith("kernel_stats.csv"):
+            stats = rows
+    lib = [r for r in stats if "ssm::" in r["Name"]]
+    if not lib:
+        raise SystemExit(f"no library kernels in the trace under {src}")
+    avg_us = {_short_kernel(r["Name"]): float(r["AverageNs"]) / 1e3 for r in lib}
+    dominant = max(lib, key=lambda r: float(r["TotalDurationNs"]))
+
+    # HBM counters, calibrated by a plain copy of known size
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        per = _pmc_per_dispatch(os.path.join(args.profile_calib, f"pmc_{c}"))
+        cal[c] = max(v.get(c, 0.0) for k, v in per.items() if "copyBuffer" in k)
+    calib_kib = 512 * 1024
+    fetch_factor, write_factor = calib_kib / cal["FETCH_SIZE"], calib_kib / cal["WRITE_SIZE"]
+    cnt = {c: _pmc_per_dispatch(os.path.join(src, f"pmc_{c}")) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    case = make_config(args.workload)
+    abytes = algorithmic_bytes(case) + (case.dim * (args.conv + 1) * 4 if args.conv else 0)
+
+    w = 70
+    out = [f"# rocprofv3 summary: {what}, workload {args.workload}{' (' + variant[1:] + ')' if variant else ''}",
+           "# made on one MI355X (gfx950)",
+           "# commands (run from /tmp with TMPDIR=/tmp, repo at /root/repo; text made by",
+           f"#   python3 bench.py --profile-summary <out> --profile-calib <calib> --profile-tag {tag} {wl_args}):"]
+    out += [f"#   {c}" for c in cmds]
+    out += ["", "## kernel trace (--kernel-trace --stats), durations in microseconds",
+            f"{'kernel':<{w}} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
+    for r in stats:
+        out.append(f"{_short_kernel(r['Name'])[:w]:<{w}} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                   f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} {float(r['Percentage']):>6.1f}")
+    out += ["", "## HBM counters per dispatch (KiB as reported; calibrated by a plain 512 MiB copy)",
+            f"copy kernel FETCH_SIZE {cal['FETCH_SIZE']:.0f} KiB for {calib_kib} KiB read  -> factor {fetch_factor:.3f}",
+            f"copy kernel WRITE_SIZE {cal['WRITE_SIZE']:.0f} KiB for {calib_kib} KiB written -> factor {write_factor:.3f}"]
+    total = 0.0
+    for k in sorted(cnt["FETCH_SIZE"]):
+        if "ssm::" not in k:
+            continue
+        fk = cnt["FETCH_SIZE"][k]["FETCH_SIZE"]
+        wk = cnt["WRITE_SIZE"].get(k, {}).get("WRITE_SIZE", 0.0)
+        fb, wb = fk * 1024 * fetch_factor, wk * 1024 * write_factor
+        total += fb + wb
+        out.append(f"{_short_kernel(k)[:w]:<{w}} FETCH {fk:>10.0f} KiB -> {fb / 1e6:>8.2f} MB   "
+                   f"WRITE {wk:>10.0f} KiB -> {wb / 1e6:>8.2f} MB")
+    out.append(f"HBM bytes per call (all library kernels of one call): {total / 1e6:.2f} MB; algorithmic bytes "
+               f"{abytes / 1e6:.2f} MB; ratio {total / abytes:.3f}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{prefix}_{tag}.txt"), "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    rec = {"workload": args.workload, "options": variant[1:], "kernel_source_hash": kernel_source_hash(args.workload),
+           "hbm_bytes_per_launch": total, "algorithmic_bytes_per_launch": abytes, "fetch_factor": fetch_factor,
+           "write_factor": write_factor, "kernel_avg_us": avg_us}
+    with open(os.path.join(ROOT, "profiles", f"pmc_{args.workload}{variant}.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+
+    # SQ counters of the dominant kernel, if the three passes were taken
+    if not all(os.path.isdir(os.path.join(src, f"sq{i}")) for i in (1, 2, 3)):
+        return
+    kname = dominant["Name"]
+    sq = {}
+    for i in (1, 2, 3):
+        sq.update(_pmc_per_dispatch(os.path.join(src, f"sq{i}")).get(kname, {}))
+    kus = float(dominant["AverageNs"]) / 1e3
+    cyc = sq["GRBM_GUI_ACTIVE"] / 8.0            # per-XCD clock cycles of the dispatch
+    simds, cus = CUS * SIMDS, CUS
+    waves = sq["SQ_WAVES"]
+    sq_cmds = [f"rocprofv3 --pmc {p} -f csv -d <out>/sq{i + 1} -o pmc -- {bench_cmd} {wl_args} --steps 3 --warmup 1 "
+               f"--rotate 1 --no-cpu-baseline" for i, p in enumerate(SQ_PASSES)]
+    lines = [f"# SQ / GRBM counters per dispatch of {_short_kernel(kname)}, workload {args.workload}{variant}",
+             "# made on one MI355X (gfx950); counter units as rocprofv3 reports them",
+             "# commands (from /tmp with TMPDIR=/tmp, repo at /root/repo), three passes:"]
+    lines += [f"#   {c}" for c in sq_cmds]
+    lines.append("")
+    lines += [f"{k:<28} {v:>14.6g}" for k, v in sorted(sq.items())]
+    mf = sq.get("SQ_INSTS_MFMA", 0.0)
+    lines += ["", "derived (GRBM_GUI_ACTIVE sums the 8 XCDs; SQ_ACTIVE_*, SQ_WAIT_*, SQ_WAVE_CYCLES are in quad-cycles):",
+              f"  shader clock over the dispatch   {cyc / (kus * 1e3):.2f} GHz  (GRBM_GUI_ACTIVE/8 over the {kus:.1f} us "
+              f"average of the kernel trace)",
+              f"  VALU instructions per wave       {sq['SQ_INSTS_VALU'] / waves:.0f}  "
+              f"({100 * sq['SQ_INSTS_VALU_TRANS_F32'] / sq['SQ_INSTS_VALU']:.0f}% transcendental)",
+              f"  VALU busy per SIMD               {100 * 4 * sq['SQ_ACTIVE_INST_VALU'] / (simds * cyc):.0f}%  "
+              f"(4*SQ_ACTIVE_INST_VALU / ({simds} SIMDs x cycles))",
+              f"  cycles per VALU instruction      {4 * sq['SQ_ACTIVE_INST_VALU'] / sq['SQ_INSTS_VALU']:.2f}  "
+              f"(per wave, issue to completion)",
+              f"  LDS instructions per wave        {sq['SQ_INSTS_LDS'] / waves:.0f};  LDS busy per CU "
+              f"{100 * 4 * sq['SQ_ACTIVE_INST_LDS'] / (cus * cyc):.0f}% of wave-cycles summed over its 4 SIMDs",
+              f"  LDS bank-conflict cycles         "
+              f"{100 * sq['SQ_LDS_BANK_CONFLICT'] / max(1.0, 4 * sq['SQ_ACTIVE_INST_LDS']):.0f}% of LDS-active cycles",
+              f"  wave time waiting to issue       {100 * sq['SQ_WAIT_INST_ANY'] / sq['SQ_WAVE_CYCLES']:.0f}% (any), "
+              f"{100 * sq['SQ_WAIT_INST_LDS'] / sq['SQ_WAVE_CYCLES']:.0f}% (LDS)",
+              f"  wave time waiting (s_waitcnt)    {100 * sq['SQ_WAIT_ANY'] / sq['SQ_WAVE_CYCLES']:.0f}%",
+              f"  SALU instructions per wave       {sq['SQ_INSTS_SALU'] / waves:.0f}"]
+    if mf:
+        lines += [f"  MFMA instructions per wave       {mf / waves:.0f};  MFMA busy per SIMD "
+                  f"{100 * sq['SQ_VALU_MFMA_BUSY_CYCLES'] / (simds * cyc):.0f}%",
+                  f"    (SQ_VALU_MFMA_BUSY_CYCLES / ({simds} SIMDs x cycles); the counter sums the SIMDs: it equals",
+                  f"     SQ_INSTS_MFMA x {sq['SQ_VALU_MFMA_BUSY_CYCLES'] / mf:.1f} cycles per 16x16x32 bf16 MFMA)"]
+    with open(os.path.join(ROOT, "profiles", f"sq_counters_{tag}.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,7 +562,15 @@ def main():
     ap.add_argument("--valu-rates", action="store_true",
                     help="measure the fp32 / transcendental issue rates, clock and HBM stream rates the "
                          "rooflines rest on (libssm_rates.so), print one JSON line per measurement, then exit")
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="summarise the rocprofv3 CSV output under DIR into profiles/ (no GPU), then exit")
+    ap.add_argument("--profile-calib", metavar="DIR", help="calibration copy counters for --profile-summary")
+    ap.add_argument("--profile-tag", help="name of the summary files (default: the workload)")
     args = ap.parse_args()
+
+    if args.profile_summary:
+        args.profile_tag = args.profile_tag or args.workload
+        return profile_summary(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (the scan shards over "
