@@ -128,7 +128,8 @@ def scan_f64(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, 
 
     discretization: "euler" (B̄ = Δ·B) or "zoh" (exact zero-order hold, B̄ = expm1(ΔA)/A·B).
     conv_w (D, K) [, conv_b (D,), conv_state_in (B, D, K-1)]: u is the raw input of a causal
-    depthwise convolution followed by SiLU ((B,D,L) layout only).
+    depthwise convolution along time followed by SiLU, per channel d (d = h*P + p in the
+    multi-head layout).
     """
     lay = LAYOUT_BDL if layout == "bdl" else LAYOUT_BLHP
     iod = 1 if io_dtype == "bf16" else 0
@@ -198,13 +199,18 @@ def scan_numpy_f64(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=
     if conv_w is not None:                                            # causal depthwise conv + SiLU on u
         w = np.asarray(conv_w, np.float64)                            # (D, K)
         K = w.shape[1]
-        Bsz_, Dm_, L_ = u.shape
+        if layout == "bdl":
+            xs = u                                                    # (B, D, L)
+        else:                                                         # (B, L, H, P) -> (B, D, L), d = h*P + p
+            xs = u.reshape(u.shape[0], u.shape[1], -1).transpose(0, 2, 1)
+        Bsz_, Dm_, L_ = xs.shape
         left = np.zeros((Bsz_, Dm_, K - 1)) if conv_state_in is None else np.asarray(conv_state_in, np.float64)
-        xp = np.concatenate([left, u], axis=2)                        # (B, D, K-1+L)
-        c = np.zeros_like(u) + (0.0 if conv_b is None else np.asarray(conv_b, np.float64)[None, :, None])
+        xp = np.concatenate([left, xs], axis=2)                       # (B, D, K-1+L)
+        c = np.zeros_like(xs) + (0.0 if conv_b is None else np.asarray(conv_b, np.float64)[None, :, None])
         for k in range(K):
             c = c + w[None, :, k:k + 1] * xp[:, :, k:k + L_]
-        u = c / (1.0 + np.exp(-c))
+        xs = c / (1.0 + np.exp(-c))
+        u = xs if layout == "bdl" else np.ascontiguousarray(xs.transpose(0, 2, 1)).reshape(u.shape)
     A = np.asarray(A, np.float64)
     if layout == "bdl":
         Bsz, Dm, L = u.shape

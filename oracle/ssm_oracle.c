@@ -206,7 +206,8 @@ int oracle_scan_f64(const void* u, const void* delta, const float* A, const void
  * convolution (weights (D, conv_k) float32, bias (D) or NULL) and SiLU; the
  * conv_k - 1 inputs before t = 0 come from conv_state_in (B, D, conv_k-1) or
  * are 0, and conv_state_out (B, D, conv_k-1) receives the last conv_k - 1 raw
- * inputs.  Only the (B,D,L) layout; conv_k in 1..16.
+ * inputs.  Both layouts: the convolution runs along time per channel d (d = h*P + p
+ * in the multi-head layout, whose x is read at (b, t, h, p)); conv_k in 1..16.
  */
 int oracle_conv_scan_f64(const void* u, const float* conv_w, const float* conv_b, int conv_k,
                          const float* conv_state_in, double* conv_state_out, const void* delta, const float* A,
@@ -214,7 +215,7 @@ int oracle_conv_scan_f64(const void* u, const float* conv_w, const float* conv_b
                          int softplus, const float* h0, const oracle_dims* dims, const int64_t* t_out,
                          int64_t n_t_out, double* y, double* h_last, int nthreads) {
   if (!u || !delta || !A || !B || !C || !dims || !y) return -1;
-  if (conv_k < 0 || conv_k > 16 || (conv_k > 0 && (!conv_w || dims->layout != 0))) return -1;
+  if (conv_k < 0 || conv_k > 16 || (conv_k > 0 && !conv_w)) return -1;
   const oracle_dims m = *dims;
   if (m.batch <= 0 || m.seqlen <= 0 || m.dim <= 0 || m.dstate <= 0 || m.ngroups <= 0) return -1;
   if (m.discretization != 0 && m.discretization != 1) return -1;

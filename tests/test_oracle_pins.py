@@ -705,9 +705,11 @@ def test_conv_continuation_bitwise():
     np.testing.assert_allclose(h2, h, rtol=1e-6, atol=1e-7)
 
 
-def test_conv_c_and_numpy_twins_agree():
-    c = make_case(layout="bdl", io_dtype="bf16", batch=2, seqlen=45, dim=6, dstate=7, seed=23, has_h0=True,
-                  A_kind="lognormal")
+@pytest.mark.parametrize("layout", ["bdl", "blhp"])
+def test_conv_c_and_numpy_twins_agree(layout):
+    shape = dict(dim=6) if layout == "bdl" else dict(dim=6, nheads=2, headdim=3)
+    c = make_case(layout=layout, io_dtype="bf16", batch=2, seqlen=45, dstate=7, seed=23, has_h0=True,
+                  A_kind="lognormal", **shape)
     rng = np.random.default_rng(4)
     w = rng.normal(size=(6, 4)).astype(np.float32)
     b = rng.normal(size=(6,)).astype(np.float32)
@@ -721,3 +723,58 @@ def test_conv_c_and_numpy_twins_agree():
                                    conv_state_in=st)
     np.testing.assert_allclose(yc, yn, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(hc, hn, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("K", [1, 3, 4])
+def test_conv_stage_matches_numpy_convolve_multihead(K):
+    """Multi-head layout, C = 0 and D = 1: y[b, t, h, p] is the stage alone, SiLU of the
+    causal convolution of channel d = h*P + p over time (numpy.convolve on that channel's
+    series, taken out of the (B, L, H, P) array), with the carried inputs in front."""
+    rng = np.random.default_rng(31 + K)
+    Bsz, L, H, P, N = 2, 29, 3, 4, 5
+    x = rng.normal(size=(Bsz, L, H, P)).astype(np.float32)
+    w = rng.normal(size=(H * P, K)).astype(np.float32)
+    b = rng.normal(size=(H * P,)).astype(np.float32)
+    st = rng.normal(size=(Bsz, H * P, K - 1)).astype(np.float32)
+    steps = rng.uniform(0.01, 0.2, size=(Bsz, L, H)).astype(np.float32)
+    A = -rng.uniform(0.5, 2.0, size=(H,)).astype(np.float32)
+    Bm = rng.normal(size=(Bsz, L, 1, N)).astype(np.float32)
+    y, _, cs = oracle.scan_f64(x, steps, A, Bm, np.zeros_like(Bm), np.ones(H * P, np.float32), None, None, False,
+                               None, layout="blhp", conv_w=w, conv_b=b, conv_state_in=st, want_conv_state=True)
+    for bb in range(Bsz):
+        for h in range(H):
+            for q in range(P):
+                d = h * P + q
+                series = np.concatenate([st[bb, d], x[bb, :, h, q]]).astype(np.float64)
+                c = np.convolve(series, w[d, ::-1].astype(np.float64))[K - 1:K - 1 + L] + b[d]
+                np.testing.assert_allclose(y[bb, :, h, q], c / (1.0 + np.exp(-c)), rtol=1e-13, atol=1e-14)
+                np.testing.assert_array_equal(cs[bb, d], series[L:])            # the last K-1 raw inputs
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_conv_multihead_layout_equivalence(io):
+    """P-i with the input stage: a multi-head run with the conv stage equals the (B,D,L) run
+    on the transposed inputs, bit for bit (y, final state and conv state)."""
+    H, P, N, L, Bsz, G, K = 4, 3, 6, 40, 2, 2, 4
+    c = make_case(layout="blhp", io_dtype=io, batch=Bsz, seqlen=L, dim=H * P, dstate=N, nheads=H, headdim=P,
+                  ngroups=G, seed=15, has_z=True, has_h0=True)
+    rng = np.random.default_rng(8)
+    w = rng.normal(size=(H * P, K)).astype(np.float32)
+    b = rng.normal(size=(H * P,)).astype(np.float32)
+    st = rng.normal(size=(Bsz, H * P, K - 1)).astype(np.float32)
+    y, h, cs = run_case(c, conv_w=w, conv_b=b, conv_state_in=st, want_conv_state=True)
+    T = c.tensors
+    u = T["u"].permute(0, 2, 3, 1).reshape(Bsz, H * P, L).contiguous()
+    z = T["z"].permute(0, 2, 3, 1).reshape(Bsz, H * P, L).contiguous()
+    dl = T["delta"].permute(0, 2, 1).repeat_interleave(P, dim=1).contiguous()
+    Bm = T["B"].permute(0, 2, 3, 1).contiguous()
+    Cm = T["C"].permute(0, 2, 3, 1).contiguous()
+    A = T["A"].repeat_interleave(P)[:, None].repeat(1, N).contiguous()
+    bias = T["delta_bias"].repeat_interleave(P).contiguous()
+    y2, h2, cs2 = oracle.scan_f64(np_io(u, io), np_io(dl, io), A.numpy(), np_io(Bm, io), np_io(Cm, io),
+                                  T["D"].numpy(), np_io(z, io), bias.numpy(), True, T["h0"].numpy(),
+                                  io_dtype=io, ngroups=G, conv_w=w, conv_b=b, conv_state_in=st,
+                                  want_conv_state=True)
+    np.testing.assert_array_equal(y.transpose(0, 2, 3, 1).reshape(Bsz, H * P, L), y2)
+    np.testing.assert_array_equal(h, h2)
+    np.testing.assert_array_equal(cs, cs2)
