@@ -625,7 +625,7 @@ def main():
         if conv is not None:
             scan.ssm_conv_scan_fwd(T["u"], conv[0], conv[1], T["delta"], T["A"], T["B"], T["C"], T["D"], T["z"],
                                    T["delta_bias"], case.softplus, T["h0"], discretization=args.discretization,
-                                   stream=stream)
+                                   layout=case.layout, stream=stream)
             return
         scan.ssm_scan_fwd(T["u"], T["delta"], T["A"], T["B"], T["C"], T["D"], T["z"], T["delta_bias"],
                           case.softplus, T["h0"], layout=case.layout, y=y, h_last=h, workspace=ws, stream=stream,

@@ -156,9 +156,12 @@ typedef struct ssm_conv {
 } ssm_conv_t;
 
 /*
- * ssm_scan_fwd with the input stage above; x has the layout and dtype of u.
+ * ssm_scan_fwd with the input stage above; x has the layout and dtype of u, and
+ * channel d of weight, bias and the states is h*headdim + p in SSM_LAYOUT_BLHP.
  * Supported for SSM_LAYOUT_BDL with dstate <= 32 and seqlen <= 2^26 (the
- * per-channel kernels); other shapes return SSM_ERR_UNSUPPORTED.  conv or conv->weight NULL:
+ * per-channel kernels) and for SSM_LAYOUT_BLHP with bfloat16 storage, dstate in
+ * {32, 64, 128} and headdim a multiple of 16 (the chunked kernel); other shapes
+ * return SSM_ERR_UNSUPPORTED.  conv or conv->weight NULL:
  * SSM_ERR_NULL_ARG; width outside 1..4: SSM_ERR_UNSUPPORTED.  state_out must
  * not overlap any input or output.  Workspace, stream and errors as for
  * ssm_scan_fwd (ssm_scan_workspace_size gives the scratch size).

@@ -317,8 +317,8 @@ static int scan_entry(const void* u, const ssm_conv_t* conv, const void* delta, 
   if (conv) {
     if (!conv->weight) return SSM_ERR_NULL_ARG;
     if (conv->width < 1 || conv->width > 4 || conv->reserved != 0) return SSM_ERR_UNSUPPORTED;
-    // the fused stage lives in the per-channel (row-group) kernels
-    if (pl.kernel != 1 && pl.kernel != 5 && pl.kernel != 6) return SSM_ERR_UNSUPPORTED;
+    // the fused stage lives in the per-channel (row-group) kernels and the chunked multi-head kernel
+    if (pl.kernel != 1 && pl.kernel != 5 && pl.kernel != 6 && pl.kernel != 2) return SSM_ERR_UNSUPPORTED;
     const void* cps[] = {conv->weight, conv->bias, conv->state_in, conv->state_out};
     for (const void* q : cps)
       if (ssm::misaligned(q)) return SSM_ERR_ALIGN;

@@ -32,6 +32,12 @@
 // each group of 16 lanes, lane i receives element i % 4 of the 8-byte pieces addressed by
 // lanes 4k + i/4 (k = 0..3), so with lane j addressing row k0 + j/4, columns 4(j%4)..+3
 // of a [k][r] array, lane i gets column i of rows k0 .. k0+3.
+//
+// Optional input stage (CONV): u is SiLU of a causal depthwise convolution (width K <= 4,
+// filter right-aligned in 4 taps) of the raw input x along time, per channel d = h P + p
+// («AI底层架构的一场革命», section "Mamba Block：完整模块结构").  The thread that stages
+// X = dt u for (step s, 8 positions) also loads x at s-1, s-2, s-3 (the carried state
+// before t = 0), convolves, and leaves u in LDS, where the output step reads it for D u.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -123,7 +129,7 @@ __device__ __forceinline__ bf16x8 ld8_tr_halves(const uint16_t* base, int k0, in
 // the state each segment before the last reaches from zero, and its decay e^{A sum dt},
 // the chunk-carry form of the scan operator of «Mamba 选择性状态空间模型» §4.1); the
 // main pass (MODE 0) folds the aggregates of the preceding segments into its initial state.
-template <int N, int PS, bool ZOH, int MODE>
+template <int N, int PS, bool ZOH, int MODE, bool CONV>
 __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   constexpr int Q = 64;
   // Row strides (elements).  With 16-lane passes, a row stride of 16 B times an odd number
@@ -148,6 +154,9 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sH[2][PS * NP];     // state [p][n], hi / lo
   __shared__ float sCum[4][Q];                                         // per wave: cum (log2 units)
   __shared__ float sDt[4][Q];                                          // per wave: step sizes
+  constexpr int UP = PS + 4;                                           // row stride of sU
+  __shared__ __attribute__((aligned(16))) float sU[CONV && MODE == 0 ? Q * UP : 4];   // u = SiLU(conv x) [s][p]
+  __shared__ __attribute__((aligned(16))) float sW[CONV ? 5 * PS : 4];  // filter taps [4][p], then bias [p]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -173,6 +182,16 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   const int p0 = pslice * PS;
   const float A2 = p.A[hh] * kLog2e;
   const float biash = p.bias ? p.bias[hh] : 0.0f;
+  if (CONV) {   // filters of this slice's channels, right-aligned in 4 taps (read after the first barrier)
+    const int K = p.conv_k;
+    if (tid < PS) {
+      const int64_t d = (int64_t)hh * p.P + p0 + tid;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sW[m * PS + tid] = m >= 4 - K ? p.conv_w[d * K + m - (4 - K)] : 0.0f;
+      sW[4 * PS + tid] = p.conv_b ? p.conv_b[d] : 0.0f;
+    }
+    __syncthreads();
+  }
 
   // ---- the state: wave w holds state tiles k = w + 4 i (i < SPW, k < NST), tile k =
   //      (tn, tp) = (k / PT, k % PT); element (n, q) = (16 tn + 4 lq + r, 16 tp + l16)
@@ -244,6 +263,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   // of step lane.  Steps past the end load the last valid step (in-bounds, masked later).
   const int64_t last_chunk = ((L - 1) / Q) * Q;
   u32x4 pB[NBI] = {}, pC[NK] = {}, pU = {0u, 0u, 0u, 0u};
+  u32x4 pXc[3] = {};   // CONV: raw x at steps s-1, s-2, s-3 of this thread's u item
   u32x2 pUo[PT] = {}, pZo[PT] = {};
   float pDelta = 0.0f;
   // per-lane element offsets of a chunk's loads from its first step, for full chunks and
@@ -251,6 +271,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   // later); only a uniform chunk base is computed per chunk
   struct Offs {
     uint32_t B[NBI], C, X, XZ, dt;
+    int sx;   // step of this thread's u item within the chunk
   };
   auto offsets = [&](int nv) __attribute__((always_inline)) {
     Offs o;
@@ -261,7 +282,8 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
     }
     const int tC = min(16 * w + l16, nv - 1);
     o.C = (uint32_t)(tC * rowBC + 8 * lq);
-    o.X = (uint32_t)(min(tid / (PS / 8), nv - 1) * rowX + (tid % (PS / 8)) * 8);
+    o.sx = min(tid / (PS / 8), nv - 1);
+    o.X = (uint32_t)(o.sx * rowX + (tid % (PS / 8)) * 8);
     o.XZ = (uint32_t)(tC * rowX + 4 * lq);
     o.dt = (uint32_t)(min(lane, nv - 1) * H);
     return o;
@@ -276,7 +298,18 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
     for (int k = 0; k < NBI; ++k) pB[k] = *(const u32x4*)(bB + (last ? olast.B[k] : ofull.B[k]));
     const uint16_t* const bC = gC + row0 * rowBC + (int64_t)g * N + (last ? olast.C : ofull.C);
     const uint16_t* const bX = gU + row0 * rowX + colX;
-    if (tid < NUI) pU = *(const u32x4*)(bX + (last ? olast.X : ofull.X));
+    if (tid < NUI) {
+      const uint32_t ox = last ? olast.X : ofull.X;
+      pU = *(const u32x4*)(bX + ox);
+      if (CONV) {   // the 3 raw inputs before; before t = 0 a valid step is re-read (replaced later)
+        const int sx = last ? olast.sx : ofull.sx;
+#pragma unroll
+        for (int j = 1; j <= 3; ++j) {
+          const int jj = tc + sx >= j ? j : sx;
+          pXc[j - 1] = *(const u32x4*)(bX + ox - (int64_t)jj * rowX);
+        }
+      }
+    }
     if (MODE == 0) {   // C and the outputs' u and z: the main pass only
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) pC[kk] = *(const u32x4*)(bC + 32 * kk);
@@ -284,7 +317,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
       const uint16_t* const bZ = gZ + row0 * rowX + colX;
 #pragma unroll
       for (int j = 0; j < PT; ++j) {
-        pUo[j] = *(const u32x2*)(bX + oxz + 16 * j);
+        if (!CONV) pUo[j] = *(const u32x2*)(bX + oxz + 16 * j);
         pZo[j] = *(const u32x2*)(bZ + oxz + 16 * j);
       }
     }
@@ -314,6 +347,9 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
       }
     }
     const u32x4 cU = pU;
+    u32x4 cXc[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) cXc[j] = pXc[j];
     {   // every wave computes the chunk's step sizes and prefix sums itself (no barrier)
       float dt = 0.0f;
       if (lane < nval) {
@@ -348,10 +384,65 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
         dts *= fabsf(x) < 0.125f ? poly : (__builtin_amdgcn_exp2f(y) - 1.0f) * __builtin_amdgcn_rcpf(x);
       }
       const float ws = __builtin_amdgcn_exp2f(cum_end - sCum[w][s]);
+      float uv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uv[2 * i] = bf2f(cU[i] & 0xffffu);
+        uv[2 * i + 1] = bf2f(cU[i] >> 16);
+      }
+      if (CONV) {   // u = SiLU(bias + sum_m w[m] x_{s-3+m})
+        float xt[3][8];   // x at s-3, s-2, s-1
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            xt[2 - j][2 * i] = bf2f(cXc[j][i] & 0xffffu);
+            xt[2 - j][2 * i + 1] = bf2f(cXc[j][i] >> 16);
+          }
+        const int64_t ts = t0 + s;
+        if (ts < 3) {   // steps before t = 0: the carried raw inputs (or zeros)
+          const int K1 = p.conv_k - 1;
+#pragma unroll
+          for (int j = 0; j < 3; ++j) {
+            const int64_t tt = ts - 3 + j;
+            if (tt < 0) {
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const int64_t d = (int64_t)hh * P + p0 + qb + i;
+                xt[j][i] = (p.conv_sin && tt >= -(int64_t)K1) ? p.conv_sin[((int64_t)b * p.dim + d) * K1 + K1 + tt]
+                                                              : 0.0f;
+              }
+            }
+          }
+        }
+        float cw[5][8];
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+          const f32x4 lo = *(const f32x4*)&sW[m * PS + qb], hi = *(const f32x4*)&sW[m * PS + qb + 4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            cw[m][i] = lo[i];
+            cw[m][4 + i] = hi[i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float c = cw[4][i];
+          c = fmaf(cw[0][i], xt[0][i], c);
+          c = fmaf(cw[1][i], xt[1][i], c);
+          c = fmaf(cw[2][i], xt[2][i], c);
+          c = fmaf(cw[3][i], uv[i], c);
+          uv[i] = silu_s(c);
+        }
+        if (MODE == 0) {
+          *(f32x4*)&sU[s * UP + qb] = (f32x4){uv[0], uv[1], uv[2], uv[3]};
+          *(f32x4*)&sU[s * UP + qb + 4] = (f32x4){uv[4], uv[5], uv[6], uv[7]};
+        }
+      }
       uint32_t xh[4], xl[4], wh[4], wl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x0 = dts * bf2f(cU[i] & 0xffffu), x1 = dts * bf2f(cU[i] >> 16);
+        const float x0 = dts * uv[2 * i], x1 = dts * uv[2 * i + 1];
         split2(x0, x1, xh[i], xl[i]);
         split2(x0 * ws, x1 * ws, wh[i], wl[i]);
       }
@@ -424,7 +515,12 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
         }
         // y = Yd + e^{cum_t} Yo + D u, gated: 4 consecutive positions of step t
         const uint32_t u01 = cUo[j][0], u23 = cUo[j][1], z01 = cZo[j][0], z23 = cZo[j][1];
-        const float uv[4] = {bf2f(u01 & 0xffffu), bf2f(u01 >> 16), bf2f(u23 & 0xffffu), bf2f(u23 >> 16)};
+        float uv[4] = {bf2f(u01 & 0xffffu), bf2f(u01 >> 16), bf2f(u23 & 0xffffu), bf2f(u23 >> 16)};
+        if (CONV) {
+          const f32x4 uc = *(const f32x4*)&sU[t * UP + 16 * j + 4 * lq];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) uv[r] = uc[r];
+        }
         const float zv[4] = {bf2f(z01 & 0xffffu), bf2f(z01 >> 16), bf2f(z23 & 0xffffu), bf2f(z23 >> 16)};
         float yv[4];
 #pragma unroll
@@ -469,6 +565,18 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
     if (pslice == 0 && tid == 0) p.wsP[((int64_t)seg * p.batch + b) * H + hh] = __builtin_amdgcn_exp2f(lsum);
     return;
   }
+  // ---- the last K-1 raw inputs of this slice's channels, for a continuing call
+  if (CONV && p.conv_sout && seg == p.nseg - 1) {
+    const int K1 = p.conv_k - 1;
+    if (tid < PS * K1) {
+      const int q = tid / K1, j = tid % K1;
+      const int64_t d = (int64_t)hh * P + p0 + q, tt = L - K1 + j;
+      float v = 0.0f;
+      if (tt >= 0) v = bf2f(gU[((int64_t)b * L + tt) * rowX + colX + q]);
+      else if (p.conv_sin) v = p.conv_sin[((int64_t)b * p.dim + d) * K1 + K1 + tt];
+      p.conv_sout[((int64_t)b * p.dim + d) * K1 + j] = v;
+    }
+  }
   // ---- final state
   if (p.h_last && seg == p.nseg - 1) {
 #pragma unroll
@@ -485,21 +593,24 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   }
 }
 
-template <int N, int PS, bool ZOH>
+template <int N, int PS, bool ZOH, bool CONV>
 int launch_ps_z(const KParams& kp, hipStream_t st) {
   if (kp.nseg > 1) {   // aggregates of the segments before the last
-    hipLaunchKernelGGL((ssd_kernel<N, PS, ZOH, 1>), dim3(kp.P / PS, kp.H, kp.batch * (kp.nseg - 1)), dim3(256), 0, st,
-                       kp);
+    hipLaunchKernelGGL((ssd_kernel<N, PS, ZOH, 1, CONV>), dim3(kp.P / PS, kp.H, kp.batch * (kp.nseg - 1)), dim3(256),
+                       0, st, kp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
-  hipLaunchKernelGGL((ssd_kernel<N, PS, ZOH, 0>), dim3(kp.P / PS, kp.H, kp.batch * kp.nseg), dim3(256), 0, st, kp);
+  hipLaunchKernelGGL((ssd_kernel<N, PS, ZOH, 0, CONV>), dim3(kp.P / PS, kp.H, kp.batch * kp.nseg), dim3(256), 0, st,
+                     kp);
   return (int)hipGetLastError();
 }
 
 template <int N, int PS>
 int launch_ps(const KParams& kp, int zoh, hipStream_t st) {
-  return zoh ? launch_ps_z<N, PS, true>(kp, st) : launch_ps_z<N, PS, false>(kp, st);
+  if (kp.conv_k > 0)
+    return zoh ? launch_ps_z<N, PS, true, true>(kp, st) : launch_ps_z<N, PS, false, true>(kp, st);
+  return zoh ? launch_ps_z<N, PS, true, false>(kp, st) : launch_ps_z<N, PS, false, false>(kp, st);
 }
 
 template <int N>

@@ -324,30 +324,42 @@ def ssm_conv_scan_fwd(x: torch.Tensor, conv_weight: torch.Tensor, conv_bias: Opt
                       D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                       delta_bias: Optional[torch.Tensor] = None, softplus: bool = True,
                       h0: Optional[torch.Tensor] = None, *, conv_state_in: Optional[torch.Tensor] = None,
-                      want_conv_state: bool = False, discretization: str = "delta_b",
+                      want_conv_state: bool = False, discretization: str = "delta_b", layout: str = "bdl",
                       stream: Optional[torch.cuda.Stream] = None):
-    """Causal depthwise conv1d + SiLU on x, then the scan ((B, D, L) layout).  conv_weight (D, K) float32,
-    K in 1..4.  Returns (y, h_last, conv_state_out or None)."""
+    """Causal depthwise conv1d + SiLU on x along time, then the scan.  layout "bdl": x (B, D, L);
+    "blhp": x (B, L, H, P), channel d = h*P + p.  conv_weight (D, K) float32, K in 1..4.
+    Returns (y, h_last, conv_state_out or None)."""
     lib = load_library()
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("ssm_conv_scan_fwd runs on the GPU: tensors must be on a cuda device")
-    Bsz, Dm, L = x.shape
-    K = conv_weight.shape[1]
     f32 = torch.float32
+    io = x.dtype
+    if layout == "bdl":
+        Bsz, Dm, L = x.shape
+        G, N = B.shape[1], B.shape[2]
+        H, P = 0, 0
+        shapes = dict(delta=(Bsz, Dm, L), A=(Dm, N), B=(Bsz, G, N, L), bias=(Dm,))
+    elif layout == "blhp":
+        Bsz, L, H, P = x.shape
+        Dm = H * P
+        G, N = B.shape[2], B.shape[3]
+        shapes = dict(delta=(Bsz, L, H), A=(H,), B=(Bsz, L, G, N), bias=(H,))
+    else:
+        raise ValueError(layout)
+    K = conv_weight.shape[1]
     _check(conv_weight, "conv_weight", f32, (Dm, K), dev)
     _check(conv_bias, "conv_bias", f32, (Dm,), dev)
     _check(conv_state_in, "conv_state_in", f32, (Bsz, Dm, K - 1), dev)
-    io = x.dtype
-    G, N = B.shape[1], B.shape[2]
-    for t, name, dt, shp in ((delta, "delta", io, (Bsz, Dm, L)), (A, "A", f32, (Dm, N)), (B, "B", io, (Bsz, G, N, L)),
-                             (C, "C", io, (Bsz, G, N, L)), (D, "D", f32, (Dm,)), (z, "z", io, (Bsz, Dm, L)),
-                             (delta_bias, "delta_bias", f32, (Dm,)), (h0, "h0", f32, (Bsz, Dm, N))):
+    for t, name, dt, shp in ((delta, "delta", io, shapes["delta"]), (A, "A", f32, shapes["A"]),
+                             (B, "B", io, shapes["B"]), (C, "C", io, shapes["B"]), (D, "D", f32, (Dm,)),
+                             (z, "z", io, tuple(x.shape)), (delta_bias, "delta_bias", f32, shapes["bias"]),
+                             (h0, "h0", f32, (Bsz, Dm, N))):
         _check(t, name, dt, shp, dev)
     y = torch.empty_like(x)
     h_last = torch.empty((Bsz, Dm, N), dtype=f32, device=dev)
     state_out = torch.empty((Bsz, Dm, max(K - 1, 1)), dtype=f32, device=dev) if want_conv_state else None
-    dims = make_dims("bdl", "bf16" if io == torch.bfloat16 else "f32", Bsz, L, Dm, N, 0, 0, G, discretization)
+    dims = make_dims(layout, "bf16" if io == torch.bfloat16 else "f32", Bsz, L, Dm, N, H, P, G, discretization)
     need = int(lib.ssm_scan_workspace_size(ctypes.byref(dims)))
     ws = None
     if need:

@@ -225,7 +225,11 @@ def test_conv_scan_rejects_bad_arguments():
     assert callc(cv(reserved=1)) == scan.SSM_ERR_UNSUPPORTED
     assert callc(cv(), dims(dstate=64)) == scan.SSM_ERR_UNSUPPORTED                      # workgroup-kernel shape
     assert callc(cv(), scan.make_dims("blhp", "bf16", 2, 64, 128, 16, nheads=2, headdim=64)) == \
-        scan.SSM_ERR_UNSUPPORTED
+        scan.SSM_ERR_UNSUPPORTED                                                        # 16 states: scan kernel
+    assert callc(cv(), scan.make_dims("blhp", "f32", 2, 64, 128, 64, nheads=2, headdim=64)) == \
+        scan.SSM_ERR_UNSUPPORTED                                                        # float32: scan kernel
+    assert callc(cv(), scan.make_dims("blhp", "bf16", 2, 64, 128, 64, nheads=16, headdim=8)) == \
+        scan.SSM_ERR_UNSUPPORTED                                                        # head size not 16k
     assert callc(cv(state_in=P["ws"] + 4)) == scan.SSM_ERR_ALIGN
     assert callc(cv(state_out=P["u"])) == scan.SSM_ERR_ALIAS
     assert callc(cv(state_out=P["y"] + 16)) == scan.SSM_ERR_ALIAS

@@ -4,7 +4,10 @@ sequence lengths (element path), 16 and 32 states, forced time segments (the
 segment's first block reads the 3 raw inputs before it), a carried conv state in
 and out, the exact-hold discretization, a two-call continuation, and every
 16-state launch (2, 4, 8 or 16 steps per lane take their 3 earlier raw inputs
-from one or two lanes to the left, or from the carry of the previous block).
+from one or two lanes to the left, or from the carry of the previous block).  The multi-head layout (chunked kernel, bfloat16)
+convolves each channel d = h*P + p along time: 32, 64 and 128 states, 16- and 32-position
+slices, ragged last chunks, forced segments (a segment's first chunk reads the raw inputs
+before it), the exact hold, and a two-call continuation.
 Tolerances as for the scan: 1e-4 (float32) and 2e-2 (bfloat16) relative to 1 + |ref|.
 """
 import numpy as np
@@ -48,7 +51,7 @@ def run(c, w, b, st, disc="delta_b", h0=None):
     y, h, cs = scan.ssm_conv_scan_fwd(T["u"], w.to(DEV), None if b is None else b.to(DEV), T["delta"], T["A"],
                                       T["B"], T["C"], T["D"], T["z"], T["delta_bias"], c.softplus, h0,
                                       conv_state_in=None if st is None else st.to(DEV), want_conv_state=True,
-                                      discretization=disc)
+                                      discretization=disc, layout=c.layout)
     torch.cuda.synchronize()
     return y, h, cs
 
@@ -144,4 +147,76 @@ def test_conv_scan_continuation():
     y = torch.cat([y1, y2], dim=2)
     assert scaled_err(y, y_ref) <= TOL["f32"]
     assert scaled_err(h2, h_ref) <= TOL["f32"]
+    np.testing.assert_array_equal(cs2.double().cpu().numpy(), cs_ref)
+
+
+# ---------------------------------------------------------------------------
+# Multi-head layout: the chunked kernel (bfloat16 storage, 32/64/128 states)
+# ---------------------------------------------------------------------------
+
+MH_CASES = [
+    # name, shape, K, carried state, forced segments, discretization, forced 16-position slices
+    ("mh-N128-K4", dict(batch=2, seqlen=200, nheads=4, headdim=64, dstate=128), 4, True, None, "delta_b", False),
+    ("mh-N64-K3-nostate", dict(batch=1, seqlen=130, nheads=3, headdim=32, dstate=64), 3, False, None, "delta_b",
+     False),
+    ("mh-N32-P16-K2", dict(batch=2, seqlen=64, nheads=5, headdim=16, dstate=32), 2, True, None, "delta_b", False),
+    ("mh-N128-K4-segments", dict(batch=1, seqlen=700, nheads=2, headdim=64, dstate=128), 4, True, "3", "delta_b",
+     False),
+    ("mh-N64-K4-zoh", dict(batch=2, seqlen=150, nheads=2, headdim=64, dstate=64), 4, True, None, "zoh", False),
+    ("mh-N128-K1", dict(batch=1, seqlen=96, nheads=2, headdim=32, dstate=128), 1, False, None, "delta_b", False),
+    ("mh-N128-K4-ps16", dict(batch=1, seqlen=190, nheads=2, headdim=64, dstate=128), 4, True, None, "delta_b", True),
+    ("mh-N64-K4-short", dict(batch=2, seqlen=2, nheads=2, headdim=32, dstate=64), 4, True, None, "delta_b", False),
+    ("mh-N128-K3-groups", dict(batch=1, seqlen=160, nheads=4, headdim=32, dstate=128, ngroups=2), 3, True, "2",
+     "delta_b", False),
+]
+
+
+def mh_case(name, kw, seed):
+    kw = dict(kw)
+    kw["dim"] = kw["nheads"] * kw["headdim"]
+    return make_case(name, layout="blhp", io_dtype="bf16", seed=seed, has_h0=True, A_kind="head_uniform", **kw)
+
+
+@pytest.mark.parametrize("name,kw,K,with_state,segs,disc,ps16", MH_CASES, ids=[c[0] for c in MH_CASES])
+def test_conv_scan_multihead(name, kw, K, with_state, segs, disc, ps16, monkeypatch):
+    if segs:
+        monkeypatch.setenv("SSM_SCAN_SEGMENTS", segs)
+    if ps16:
+        monkeypatch.setenv("SSM_SSD_PS", "16")
+    c = mh_case(name, kw, 71)
+    dims = scan.make_dims("blhp", "bf16", c.batch, c.seqlen, c.dim, c.dstate, c.nheads, c.headdim, c.ngroups)
+    plan = scan.describe(dims)
+    assert "kernel=ssd" in plan
+    w, b, st = conv_params(c.dim, K, c.batch, 72, with_state)
+    print(f"[gpu] conv scan {name} K={K} state={with_state} segments={segs} disc={disc} plan={plan}", flush=True)
+    y, h, cs = run(c, w, b, st, disc)
+    y_ref, h_ref, cs_ref = ref(c, w, b, st, "zoh" if disc == "zoh" else "euler")
+    ey, eh = scaled_err(y, y_ref), scaled_err(h, h_ref)
+    print(f"[gpu]   max scaled err y {ey:.2e} h {eh:.2e}", flush=True)
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    np.testing.assert_array_equal(cs.double().cpu().numpy(), cs_ref)
+
+
+def test_conv_scan_multihead_continuation():
+    c = mh_case("mh-cont", dict(batch=2, seqlen=256, nheads=2, headdim=64, dstate=128), 75)
+    w, b, st = conv_params(c.dim, 4, c.batch, 76, True)
+    print("[gpu] conv scan multi-head continuation", flush=True)
+    y_ref, h_ref, cs_ref = ref(c, w, b, st)
+    k = 100                                       # not a multiple of the 64-step chunk
+    T = c.tensors
+    parts = []
+    for lo, hi in ((0, k), (k, c.seqlen)):
+        cc = mh_case("p", dict(batch=2, seqlen=hi - lo, nheads=2, headdim=64, dstate=128), 75)
+        for key in ("u", "delta", "z", "B", "C"):
+            cc.tensors[key] = T[key][:, lo:hi].contiguous()
+        for key in ("A", "D", "delta_bias"):
+            cc.tensors[key] = T[key]
+        parts.append(cc)
+    parts[0].tensors["h0"] = T["h0"]
+    y1, h1, cs1 = run(parts[0], w, b, st)
+    parts[1].tensors["h0"] = None
+    y2, h2, cs2 = run(parts[1], w, b, cs1.cpu(), h0=h1)
+    y = torch.cat([y1, y2], dim=1)
+    assert scaled_err(y, y_ref) <= TOL["bf16"]
+    assert scaled_err(h2, h_ref) <= TOL["bf16"]
     np.testing.assert_array_equal(cs2.double().cpu().numpy(), cs_ref)
