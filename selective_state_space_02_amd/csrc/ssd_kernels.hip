@@ -35,9 +35,11 @@
 //
 // Optional input stage (CONV): u is SiLU of a causal depthwise convolution (width K <= 4,
 // filter right-aligned in 4 taps) of the raw input x along time, per channel d = h P + p
-// («AI底层架构的一场革命», section "Mamba Block：完整模块结构").  The thread that stages
-// X = dt u for (step s, 8 positions) also loads x at s-1, s-2, s-3 (the carried state
-// before t = 0), convolves, and leaves u in LDS, where the output step reads it for D u.
+// («AI底层架构的一场革命», section "Mamba Block：完整模块结构").  Each lane of a wave that
+// stages u items convolves 2 channels x 4 consecutive steps of the wave's steps: it keeps
+// its 2 filters in registers, loads the 7 raw inputs its 4 steps need (2 channels per
+// 4-byte load; the carried state before t = 0), and leaves u in LDS, where the wave's own
+// X = dt u staging and the output step's D u read it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -155,8 +157,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   __shared__ float sCum[4][Q];                                         // per wave: cum (log2 units)
   __shared__ float sDt[4][Q];                                          // per wave: step sizes
   constexpr int UP = PS + 4;                                           // row stride of sU
-  __shared__ __attribute__((aligned(16))) float sU[CONV && MODE == 0 ? Q * UP : 4];   // u = SiLU(conv x) [s][p]
-  __shared__ __attribute__((aligned(16))) float sW[CONV ? 5 * PS : 4];  // filter taps [4][p], then bias [p]
+  __shared__ __attribute__((aligned(16))) float sU[CONV ? Q * UP : 4];   // u = SiLU(conv x) [s][p]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -182,15 +183,23 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   const int p0 = pslice * PS;
   const float A2 = p.A[hh] * kLog2e;
   const float biash = p.bias ? p.bias[hh] : 0.0f;
-  if (CONV) {   // filters of this slice's channels, right-aligned in 4 taps (read after the first barrier)
+  // CONV: this lane's items, channels p0 + cpos, + 1 at steps cs0 .. cs0 + 3 of each chunk: the
+  // wave stages the u items of steps [w CSW, (w + 1) CSW), CSW = 512 / PS (at PS = 16 waves 2
+  // and 3 stage none); the filters (right-aligned in 4 taps) and biases stay in registers
+  constexpr int CSW = 512 / PS;
+  const int cpos = 2 * (lane % (PS / 2));
+  const int cs0 = w * CSW + 4 * (lane / (PS / 2));
+  const bool conv_lane = CONV && w * CSW < Q;
+  float cwt[2][5] = {};
+  if (CONV) {
     const int K = p.conv_k;
-    if (tid < PS) {
-      const int64_t d = (int64_t)hh * p.P + p0 + tid;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) sW[m * PS + tid] = m >= 4 - K ? p.conv_w[d * K + m - (4 - K)] : 0.0f;
-      sW[4 * PS + tid] = p.conv_b ? p.conv_b[d] : 0.0f;
+    for (int q = 0; q < 2; ++q) {
+      const int64_t d = (int64_t)hh * p.P + p0 + cpos + q;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) cwt[q][m] = m >= 4 - K ? p.conv_w[d * K + m - (4 - K)] : 0.0f;
+      cwt[q][4] = p.conv_b ? p.conv_b[d] : 0.0f;
     }
-    __syncthreads();
   }
 
   // ---- the state: wave w holds state tiles k = w + 4 i (i < SPW, k < NST), tile k =
@@ -263,7 +272,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
   // of step lane.  Steps past the end load the last valid step (in-bounds, masked later).
   const int64_t last_chunk = ((L - 1) / Q) * Q;
   u32x4 pB[NBI] = {}, pC[NK] = {}, pU = {0u, 0u, 0u, 0u};
-  u32x4 pXc[3] = {};   // CONV: raw x at steps s-1, s-2, s-3 of this thread's u item
+  uint32_t pXt[7] = {};   // CONV: raw x of this lane's 2 channels at steps cs0 - 3 .. cs0 + 3
   u32x2 pUo[PT] = {}, pZo[PT] = {};
   float pDelta = 0.0f;
   // per-lane element offsets of a chunk's loads from its first step, for full chunks and
@@ -298,16 +307,15 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
     for (int k = 0; k < NBI; ++k) pB[k] = *(const u32x4*)(bB + (last ? olast.B[k] : ofull.B[k]));
     const uint16_t* const bC = gC + row0 * rowBC + (int64_t)g * N + (last ? olast.C : ofull.C);
     const uint16_t* const bX = gU + row0 * rowX + colX;
-    if (tid < NUI) {
-      const uint32_t ox = last ? olast.X : ofull.X;
-      pU = *(const u32x4*)(bX + ox);
-      if (CONV) {   // the 3 raw inputs before; before t = 0 a valid step is re-read (replaced later)
-        const int sx = last ? olast.sx : ofull.sx;
+    if (tid < NUI && !CONV) pU = *(const u32x4*)(bX + (last ? olast.X : ofull.X));
+    if (conv_lane) {   // steps before t = 0 re-read step 0, past the end the last step (replaced / masked)
+      const int nv = last ? (int)(L - last_chunk) : Q;
 #pragma unroll
-        for (int j = 1; j <= 3; ++j) {
-          const int jj = tc + sx >= j ? j : sx;
-          pXc[j - 1] = *(const u32x4*)(bX + ox - (int64_t)jj * rowX);
-        }
+      for (int i = 0; i < 7; ++i) {
+        int st = cs0 - 3 + i;
+        if (tc + st < 0) st = (int)-tc;
+        if (st > nv - 1) st = nv - 1;
+        pXt[i] = *(const uint32_t*)(bX + (int64_t)st * rowX + cpos);
       }
     }
     if (MODE == 0) {   // C and the outputs' u and z: the main pass only
@@ -347,9 +355,41 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
       }
     }
     const u32x4 cU = pU;
-    u32x4 cXc[3];
+    if (conv_lane) {   // u of this lane's 2 channels x 4 steps, into LDS for the wave's X staging
+      float xw[2][7];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) cXc[j] = pXc[j];
+      for (int i = 0; i < 7; ++i) {
+        xw[0][i] = bf2f(pXt[i] & 0xffffu);
+        xw[1][i] = bf2f(pXt[i] >> 16);
+      }
+      if (t0 + cs0 < 3) {   // steps before t = 0: the carried raw inputs (or zeros)
+        const int K1 = p.conv_k - 1;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const int64_t tt = t0 + cs0 - 3 + i;
+          if (tt < 0) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int64_t d = (int64_t)hh * P + p0 + cpos + q;
+              xw[q][i] = (p.conv_sin && tt >= -(int64_t)K1) ? p.conv_sin[((int64_t)b * p.dim + d) * K1 + K1 + tt]
+                                                            : 0.0f;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float uq[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float c = cwt[q][4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) c = fmaf(cwt[q][m], xw[q][j + m], c);
+          uq[q] = silu_s(c);
+        }
+        *(float2*)&sU[(cs0 + j) * UP + cpos] = make_float2(uq[0], uq[1]);
+      }
+    }
     {   // every wave computes the chunk's step sizes and prefix sums itself (no barrier)
       float dt = 0.0f;
       if (lane < nval) {
@@ -390,53 +430,12 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(KParams p) {
         uv[2 * i] = bf2f(cU[i] & 0xffffu);
         uv[2 * i + 1] = bf2f(cU[i] >> 16);
       }
-      if (CONV) {   // u = SiLU(bias + sum_m w[m] x_{s-3+m})
-        float xt[3][8];   // x at s-3, s-2, s-1
+      if (CONV) {   // u from this wave's conv lanes
+        const f32x4 lo = *(const f32x4*)&sU[s * UP + qb], hi = *(const f32x4*)&sU[s * UP + qb + 4];
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            xt[2 - j][2 * i] = bf2f(cXc[j][i] & 0xffffu);
-            xt[2 - j][2 * i + 1] = bf2f(cXc[j][i] >> 16);
-          }
-        const int64_t ts = t0 + s;
-        if (ts < 3) {   // steps before t = 0: the carried raw inputs (or zeros)
-          const int K1 = p.conv_k - 1;
-#pragma unroll
-          for (int j = 0; j < 3; ++j) {
-            const int64_t tt = ts - 3 + j;
-            if (tt < 0) {
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                const int64_t d = (int64_t)hh * P + p0 + qb + i;
-                xt[j][i] = (p.conv_sin && tt >= -(int64_t)K1) ? p.conv_sin[((int64_t)b * p.dim + d) * K1 + K1 + tt]
-                                                              : 0.0f;
-              }
-            }
-          }
-        }
-        float cw[5][8];
-#pragma unroll
-        for (int m = 0; m < 5; ++m) {
-          const f32x4 lo = *(const f32x4*)&sW[m * PS + qb], hi = *(const f32x4*)&sW[m * PS + qb + 4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            cw[m][i] = lo[i];
-            cw[m][4 + i] = hi[i];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float c = cw[4][i];
-          c = fmaf(cw[0][i], xt[0][i], c);
-          c = fmaf(cw[1][i], xt[1][i], c);
-          c = fmaf(cw[2][i], xt[2][i], c);
-          c = fmaf(cw[3][i], uv[i], c);
-          uv[i] = silu_s(c);
-        }
-        if (MODE == 0) {
-          *(f32x4*)&sU[s * UP + qb] = (f32x4){uv[0], uv[1], uv[2], uv[3]};
-          *(f32x4*)&sU[s * UP + qb + 4] = (f32x4){uv[4], uv[5], uv[6], uv[7]};
+        for (int i = 0; i < 4; ++i) {
+          uv[i] = lo[i];
+          uv[4 + i] = hi[i];
         }
       }
       uint32_t xh[4], xl[4], wh[4], wl[4];
