@@ -149,7 +149,7 @@ def load_traffic(workload: str, variant: str = ""):
 
 def host_cpus():
     """The host's CPU counts beside the threads the oracle ran on: the oracle uses every core
-    this process may run on, up to the 16 a one-GPU machine grants each GPU."""
+    this process may run on, up to 16 (the host CPU share of one GPU on an 8-GPU MI355X node)."""
     try:
         usable = len(os.sched_getaffinity(0))
     except AttributeError:
