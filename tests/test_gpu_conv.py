@@ -220,3 +220,21 @@ def test_conv_scan_multihead_continuation():
     assert scaled_err(y, y_ref) <= TOL["bf16"]
     assert scaled_err(h2, h_ref) <= TOL["bf16"]
     np.testing.assert_array_equal(cs2.double().cpu().numpy(), cs_ref)
+
+
+@pytest.mark.parametrize("name", ["mamba2p8b_layer", "mamba2_multihead"])
+def test_workload_full_conv(name):
+    """Both layer workloads at full size with the K = 4 input stage, in the launch and with the
+    filters `bench.py --conv 4` times (same seeded recipe), against the oracle over every output."""
+    from selective_state_space_02_amd.inputs import make_config
+    c = make_config(name)
+    gen = torch.Generator().manual_seed(20260999)
+    w = (torch.randn(c.dim, 4, generator=gen) * 0.5).contiguous()
+    b = (torch.randn(c.dim, generator=gen) * 0.2).contiguous()
+    print(f"[gpu] conv scan full workload {name}", flush=True)
+    y, h, cs = run(c, w, b, None)
+    y_ref, h_ref, cs_ref = ref(c, w, b, None)
+    ey, eh = scaled_err(y, y_ref), scaled_err(h, h_ref)
+    print(f"[gpu]   max scaled err y {ey:.2e} h {eh:.2e}", flush=True)
+    assert ey <= TOL[c.io_dtype] and eh <= TOL[c.io_dtype]
+    np.testing.assert_array_equal(cs.double().cpu().numpy(), cs_ref)
