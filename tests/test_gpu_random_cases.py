@@ -40,9 +40,10 @@ def scaled_err(got, ref):
     return float((np.abs(got - ref) / (1.0 + np.abs(ref))).max()) if ref.size else 0.0
 
 
-def draw(rng, big):
-    layout = rng.choice(["bdl", "bdl", "bdl", "blhp"])
-    io = rng.choice(["bf16", "f32"])
+def draw(rng, big, mh_conv=False):
+    """mh_conv: only the multi-head layout through the input stage (bf16, the chunked kernel)."""
+    layout = "blhp" if mh_conv else rng.choice(["bdl", "bdl", "bdl", "blhp"])
+    io = "bf16" if mh_conv else rng.choice(["bf16", "f32"])
     B = rng.choice([1, 2, 3])
     L = rng.choice([1, 2, 7, 31, 32, 33, 64, 95, 128, 200, 257, 500, 1000] + ([2048, 3001, 4096] if big else []))
     conv, env = 0, {}
@@ -55,15 +56,19 @@ def draw(rng, big):
             conv = rng.choice([1, 2, 3, 4])
         env["SSM_SCAN_MIXED"] = rng.choice(["", "0", "1", "48"])
     else:
-        N = rng.choice([32, 64, 128, 16, 48, 256, 1])
+        N = rng.choice([32, 64, 128] if mh_conv else [32, 64, 128, 16, 48, 256, 1])
         G = rng.choice([1, 2])
         H = G * rng.choice([1, 2, 3])
-        P = rng.choice([16, 32, 48, 64, 8, 128, 3])
+        P = rng.choice([16, 32, 48, 64, 128] if mh_conv else [16, 32, 48, 64, 8, 128, 3])
         D = H * P
-        if rng.random() < 0.2:
+        if rng.random() < 0.2 and not mh_conv:
             env["SSM_SCAN_SSD"] = "0"
         if rng.random() < 0.2:
             env["SSM_SSD_PS"] = "16"
+        # the input stage runs where the chunked kernel does
+        if io == "bf16" and N in (32, 64, 128) and P % 16 == 0 and "SSM_SCAN_SSD" not in env and \
+                (mh_conv or rng.random() < 0.3):
+            conv = rng.choice([1, 2, 3, 4])
     if rng.random() < 0.3:
         env["SSM_SCAN_SEGMENTS"] = str(rng.choice([1, 2, 3, 5, 9]))
     return dict(layout=layout, io=io, B=B, L=L, D=D, N=N, G=G, H=H, P=P, conv=conv, env=env,
@@ -72,7 +77,13 @@ def draw(rng, big):
                           has_h0=rng.random() < 0.6,
                           delta_kind=rng.choice(["small", "small", "wide", "long", "zero"])),
                 softplus=rng.random() < 0.85, seed=rng.randrange(1 << 20), decode=rng.random() < 0.15,
-                inplace=rng.random() < 0.5, conv_state=rng.random() < 0.5)
+                inplace=rng.random() < 0.5, conv_state=rng.random() < 0.5) if not mh_conv else \
+        dict(layout=layout, io=io, B=B, L=L, D=D, N=N, G=G, H=H, P=P, conv=conv, env=env,
+             disc=rng.choice(["delta_b", "delta_b", "zoh"]),
+             opts=dict(has_z=rng.random() < 0.7, has_D=rng.random() < 0.8, has_bias=rng.random() < 0.8,
+                       has_h0=rng.random() < 0.6, delta_kind=rng.choice(["small", "small", "wide", "long", "zero"])),
+             softplus=rng.random() < 0.85, seed=rng.randrange(1 << 20), decode=False, inplace=False,
+             conv_state=rng.random() < 0.5)
 
 
 def run_case(k, monkeypatch):
@@ -113,7 +124,8 @@ def run_case(k, monkeypatch):
         csi = torch.randn(k["B"], k["D"], K - 1, generator=g).contiguous() if K > 1 and k["conv_state"] else None
         y, h, cs = scan.ssm_conv_scan_fwd(T["u"], cw.to(dev), cb.to(dev), T["delta"], T["A"], T["B"], T["C"], T["D"],
                                           T["z"], T["delta_bias"], c.softplus, T["h0"], discretization=k["disc"],
-                                          conv_state_in=None if csi is None else csi.to(dev), want_conv_state=True)
+                                          conv_state_in=None if csi is None else csi.to(dev), want_conv_state=True,
+                                          layout=layout)
         kw.update(conv_w=cw.numpy(), conv_b=cb.numpy(), conv_state_in=None if csi is None else csi.numpy(),
                   want_conv_state=True)
     else:
@@ -129,12 +141,13 @@ def run_case(k, monkeypatch):
     return scaled_err(y, yr), scaled_err(h, hr)
 
 
-@pytest.mark.parametrize("seed,count,big", [(7, 150, False), (23, 60, True), (41, 150, False)])
-def test_random_cases(seed, count, big, monkeypatch):
+@pytest.mark.parametrize("seed,count,big,mh_conv", [(7, 150, False, False), (23, 60, True, False),
+                                                   (41, 150, False, False), (59, 60, False, True)])
+def test_random_cases(seed, count, big, mh_conv, monkeypatch):
     rng = random.Random(seed)
     bad = []
     for i in range(count):
-        k = draw(rng, big)
+        k = draw(rng, big, mh_conv)
         print(f"[gpu] random case {seed}/{i}: {k}", flush=True)
         ey, eh = run_case(k, monkeypatch)
         tol = TOL[k["io"]]
