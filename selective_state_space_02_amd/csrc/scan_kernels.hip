@@ -618,12 +618,13 @@ __global__ void __launch_bounds__(NW * 64) scan_kernel(KParams p) {
 // Full blocks use vector loads issued one block ahead; the ragged last block of a
 // segment is loaded element by element after the main loop.
 //
-// Two launches use the same wave body: the plain one (waves of 8 lanes per channel),
-// and a mixed one for 16 states whose workgroup is 8 waves of 8 lanes per channel
-// plus 4 waves of 16 lanes per channel (80 channels).  The hardware places wave w of a
-// workgroup on the same SIMD as wave w+4, so every SIMD gets two 8-channel waves and
-// one 4-channel wave: equal work per SIMD when the channel count is a multiple of
-// 80 x 256 (the plain launch would leave 3 waves on half the SIMDs and 2 on the rest).
+// Three launches use the same wave body: the plain one (independent waves of 8 lanes per
+// channel), and two two-kind launches for 16 states whose workgroup is 4 waves of 4 (or
+// 8) lanes per channel plus 4 waves of 16 lanes per channel (80 or 48 channels).  The
+// hardware places wave w of a workgroup on the same SIMD as wave w+4, so every SIMD gets
+// one wave of each kind and the same 20 (12) channels: equal work per SIMD when the
+// channel count is a multiple of 80 x 256 (48 x 256), where the plain launch would leave
+// 3 waves on half the SIMDs and 2 on the rest.
 namespace rg {
 constexpr int TB = 32;          // steps per block
 constexpr int TP = TB + 4;      // padded LDS row stride
