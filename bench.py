@@ -488,13 +488,14 @@ def profile_summary(args) -> None:
                    f"WRITE {wk:>10.0f} KiB -> {wb / 1e6:>8.2f} MB")
     out.append(f"HBM bytes per call (all library kernels of one call): {total / 1e6:.2f} MB; algorithmic bytes "
                f"{abytes / 1e6:.2f} MB; ratio {total / abytes:.3f}")
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"{prefix}_{tag}.txt"), "w") as fh:
+    outdir = args.profile_out or os.path.join(ROOT, "profiles")
+    os.makedirs(outdir, exist_ok=True)
+    with open(os.path.join(outdir, f"{prefix}_{tag}.txt"), "w") as fh:
         fh.write("\n".join(out) + "\n")
     rec = {"workload": args.workload, "options": variant[1:], "kernel_source_hash": kernel_source_hash(args.workload),
            "hbm_bytes_per_launch": total, "algorithmic_bytes_per_launch": abytes, "fetch_factor": fetch_factor,
            "write_factor": write_factor, "kernel_avg_us": avg_us}
-    with open(os.path.join(ROOT, "profiles", f"pmc_{args.workload}{variant}.json"), "w") as fh:
+    with open(os.path.join(outdir, f"pmc_{args.workload}{variant}.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
 
@@ -540,7 +541,7 @@ def profile_summary(args) -> None:
                   f"{100 * sq['SQ_VALU_MFMA_BUSY_CYCLES'] / (simds * cyc):.0f}%",
                   f"    (SQ_VALU_MFMA_BUSY_CYCLES / ({simds} SIMDs x cycles); the counter sums the SIMDs: it equals",
                   f"     SQ_INSTS_MFMA x {sq['SQ_VALU_MFMA_BUSY_CYCLES'] / mf:.1f} cycles per 16x16x32 bf16 MFMA)"]
-    with open(os.path.join(ROOT, "profiles", f"sq_counters_{tag}.txt"), "w") as fh:
+    with open(os.path.join(outdir, f"sq_counters_{tag}.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
 
@@ -566,6 +567,7 @@ def main():
                     help="summarise the rocprofv3 CSV output under DIR into profiles/ (no GPU), then exit")
     ap.add_argument("--profile-calib", metavar="DIR", help="calibration copy counters for --profile-summary")
     ap.add_argument("--profile-tag", help="name of the summary files (default: the workload)")
+    ap.add_argument("--profile-out", metavar="DIR", help="where --profile-summary writes (default: profiles/)")
     args = ap.parse_args()
 
     if args.profile_summary:
