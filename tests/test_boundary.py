@@ -348,3 +348,24 @@ def test_noalloc_rejects_beyond_scratch_before_any_hip_call():
     assert scan.call_noalloc_raw(*args, dims(dim=0)) == scan.SSM_ERR_BAD_DIMS
     assert scan.call_noalloc_raw(None, *args[1:], dims()) == scan.SSM_ERR_NULL_ARG
     assert scan.call_noalloc_raw(*args[:9], a["u"] + 8, *args[10:], dims()) == scan.SSM_ERR_ALIGN
+
+
+def test_hip_failures_surface_as_ssm_err_hip(monkeypatch):
+    """On a host without a GPU the first HIP call of a valid call fails: the library returns
+    SSM_ERR_HIP and ssm_strerror names the failing call with HIP's text, for the library-made
+    workspace (hipMallocAsync), the allocation-free entry point's scratch lookup and a kernel
+    launch.  The pointers are not device memory, so this runs only where no GPU is visible."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("needs a host without a GPU (the arguments are not device pointers)")
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", "3")
+    d = dims(batch=1, seqlen=4096)
+    assert scan.workspace_size(d) > 0
+    rc = call(d)                                                     # workspace NULL: the library allocates
+    assert rc == scan.SSM_ERR_HIP and "hipMallocAsync" in scan.strerror(rc)
+    rc = scan.call_noalloc_raw(P["u"], P["delta"], P["A"], P["B"], P["C"], P["D"], P["z"], P["bias"], True,
+                               P["h0"], P["y"], P["h_last"], d)
+    assert rc == scan.SSM_ERR_HIP and "hipGetDevice" in scan.strerror(rc)
+    d.workspace, d.workspace_bytes = P["ws"], scan.workspace_size(d)
+    rc = call(d)                                                     # caller workspace: the launch itself fails
+    assert rc == scan.SSM_ERR_HIP and "kernel launch" in scan.strerror(rc)
