@@ -75,6 +75,13 @@ def test_side_stream_update_and_conv():
     w = (0.5 * torch.randn(640, 4, generator=g)).to(DEV)
     cargs = (K["u"], w, None, K["delta"], K["A"], K["B"], K["C"], K["D"], K["z"], K["delta_bias"], True, None)
     cy0, ch0, _ = scan.ssm_conv_scan_fwd(*cargs)
+    # the multi-head layout through the input stage (chunked kernel, time segments)
+    m = make_case("mhconv", layout="blhp", io_dtype="bf16", batch=1, seqlen=1200, dim=1024, dstate=128, nheads=16,
+                  headdim=64, seed=906)
+    M = on_device(m)
+    wm = (0.5 * torch.randn(1024, 3, generator=g)).to(DEV)
+    margs = (M["u"], wm, None, M["delta"], M["A"], M["B"], M["C"], M["D"], M["z"], M["delta_bias"], True, None)
+    my0, mh0, ms0 = scan.ssm_conv_scan_fwd(*margs, layout="blhp", want_conv_state=True)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -82,9 +89,12 @@ def test_side_stream_update_and_conv():
     clobber()
     cy1, ch1, _ = scan.ssm_conv_scan_fwd(*cargs, stream=side)
     clobber()
+    my1, mh1, ms1 = scan.ssm_conv_scan_fwd(*margs, layout="blhp", want_conv_state=True, stream=side)
+    clobber()
     torch.cuda.synchronize()
     assert torch.equal(y1, y0) and torch.equal(s1, s0)
     assert torch.equal(cy1, cy0) and torch.equal(ch1, ch0)
+    assert torch.equal(my1, my0) and torch.equal(mh1, mh0) and torch.equal(ms1, ms0)
 
 
 @pytest.mark.parametrize("name", list(CASES))
