@@ -369,3 +369,16 @@ def test_hip_failures_surface_as_ssm_err_hip(monkeypatch):
     d.workspace, d.workspace_bytes = P["ws"], scan.workspace_size(d)
     rc = call(d)                                                     # caller workspace: the launch itself fails
     assert rc == scan.SSM_ERR_HIP and "kernel launch" in scan.strerror(rc)
+
+
+def test_scratch_covers_every_workload():
+    """The allocation-free entry point's static scratch holds the workspace of every workload
+    the benchmark runs (plans are host-only: no GPU needed)."""
+    from selective_state_space_02_amd.inputs import CONFIGS
+    cap = scan.scratch_capacity()
+    for name, c in CONFIGS.items():
+        d = scan.make_dims(c["layout"], c["io_dtype"], c["batch"], c["seqlen"], c["dim"], c["dstate"],
+                           c.get("nheads", 0), c.get("headdim", 0), c.get("ngroups", 1))
+        for disc in ("delta_b", "zoh"):
+            d.discretization = scan.DISCRETIZATIONS[disc]
+            assert scan.workspace_size(d) <= cap, f"{name} ({disc}): {scan.workspace_size(d)} > {cap}"
