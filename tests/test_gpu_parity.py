@@ -296,3 +296,31 @@ def test_mixed_and_plain_agree():
     for y, h in ((y4, h4), (y5, h5)):
         torch.testing.assert_close(y.float(), y0.float(), rtol=1e-2, atol=1e-2)
         torch.testing.assert_close(h, h0, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("layout,io", [("bdl", "bf16"), ("bdl", "f32"), ("blhp", "bf16")])
+def test_many_short_sequences(layout, io):
+    """A serving-prefill shape: hundreds of batch items of a dozen steps (grid over the batch)."""
+    kw = dict(layout=layout, io_dtype=io, batch=300, seqlen=12, dstate=16 if layout == "bdl" else 64, seed=77,
+              has_h0=True)
+    if layout == "bdl":
+        kw.update(dim=64)
+    else:
+        kw.update(dim=128, nheads=2, headdim=64)
+    check_case(make_case("many_short", **kw))
+
+
+@pytest.mark.parametrize("layout,io", [("bdl", "f32"), ("bdl", "bf16"), ("blhp", "f32"), ("blhp", "bf16")])
+def test_extreme_step_inputs(layout, io):
+    """Raw steps spread over [-60, 40] within one tensor: softplus from its far tail (dt ~ 1e-26,
+    the state held) to dt ~ 40 (the state wiped out each step), with no bias."""
+    kw = dict(layout=layout, io_dtype=io, batch=2, seqlen=300, seed=78, has_h0=True, has_bias=False)
+    if layout == "bdl":
+        kw.update(dim=96, dstate=16, A_kind="lognormal")
+    else:
+        kw.update(dim=128, dstate=64, nheads=2, headdim=64)
+    c = make_case("extreme_dt", **kw)
+    g = torch.Generator().manual_seed(79)
+    raw = torch.rand(c.tensors["delta"].shape, generator=g) * 100.0 - 60.0
+    c.tensors["delta"] = raw.to(c.tensors["delta"].dtype).contiguous()
+    check_case(c)
